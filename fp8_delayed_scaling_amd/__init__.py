@@ -1,0 +1,249 @@
+"""fp8_delayed_scaling_amd -- FP8 per-tensor delayed scaling on AMD MI355X (gfx950).
+
+A thin ctypes binding of ``libfp8ds.so`` (the HIP kernels behind the C ABI of
+``include/fp8ds.h``).  Every function here has the name of its C entry point and only
+marshals arguments: it reads sizes, strides and pointers off torch tensors, picks the
+stream, calls the library and turns a non-zero status into an exception.  All arithmetic
+runs in the library's kernels; PyTorch only supplies device memory and streams.
+
+The library must be built (``__graft_entry__.build()`` or ``python -m
+fp8_delayed_scaling_amd.build``); importing this package without it raises immediately,
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = [
+    "E4M3", "E5M2", "OUT_BF16", "OUT_FP32", "Fp8dsError", "lib", "library_path",
+    "fp8ds_status_string", "fp8ds_version",
+    "fp8_cast_amax", "fp8_cast_transpose", "fp8_dbias_workspace_bytes", "fp8_dbias_cast_transpose",
+    "fp8_scale_update", "fp8_gemm_bias", "fp8_gemm_bias_chunked", "fp8_linear_fwd", "fp8_linear_bwd",
+]
+
+E4M3 = 0
+E5M2 = 1
+OUT_BF16 = 0
+OUT_FP32 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libfp8ds.so")
+
+
+class Fp8dsError(RuntimeError):
+    """A libfp8ds call returned a non-zero status."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+P = ctypes.c_void_p
+I64 = ctypes.c_int64
+I32 = ctypes.c_int32
+INT = ctypes.c_int
+SZ = ctypes.c_size_t
+
+_SIGS = {
+    "fp8ds_status_string": ([INT], ctypes.c_char_p),
+    "fp8ds_version": ([], INT),
+    "fp8_cast_amax": ([P, I64, P, INT, P, P, P, P, P], INT),
+    "fp8_cast_transpose": ([P, I64, I64, P, INT, P, P, P, P, P, P], INT),
+    "fp8_dbias_workspace_bytes": ([I64, I64], SZ),
+    "fp8_dbias_cast_transpose": ([P, I64, I64, P, INT, P, P, P, P, P, P, SZ, P], INT),
+    "fp8_scale_update": ([P, I64, I64, P, P, P, I32, P], INT),
+    "fp8_gemm_bias": ([P, INT, P, I64, P, INT, P, I64, P, P, I64, INT, I64, I64, I64, P], INT),
+    "fp8_gemm_bias_chunked": ([P, INT, P, I64, P, INT, P, I64, P, P, I64, INT, I64, I64, I64, INT, P, P], INT),
+    "fp8_linear_fwd": ([P, P, P, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, P, P, P], INT),
+    "fp8_linear_bwd": ([P, I64, I64, I64, P, P, P, P, P, P, P, SZ, P, P, P, P, P, P, INT, P], INT),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(
+                f"{library_path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+                "(the FP8 path has no fallback)")
+        L = ctypes.CDLL(library_path)
+        for name, (argtypes, restype) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = argtypes
+            fn.restype = restype
+        _lib = L
+    return _lib
+
+
+def fp8ds_status_string(status: int) -> str:
+    return lib().fp8ds_status_string(int(status)).decode()
+
+
+def fp8ds_version() -> int:
+    return int(lib().fp8ds_version())
+
+
+# ----------------------------------------------------------------------------- marshalling
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("tensor arguments must live on the GPU")
+    return t.data_ptr()
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(status: int):
+    if status != 0:
+        raise Fp8dsError(status, fp8ds_status_string(status))
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _want(t, dtypes, name, contiguous=True):
+    if t is None:
+        return
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ----------------------------------------------------------------------------- entry points
+
+def fp8_cast_amax(x, scale, fmt, out, scale_inv_out=None, amax_slot=None, noop=None, stream=None):
+    """Cast bfloat16 ``x`` to FP8 codes ``out`` with amax capture (see include/fp8ds.h)."""
+    _want(x, _BF16, "x")
+    _want(out, (torch.uint8,), "out")
+    if out.numel() != x.numel():
+        raise ValueError("out must have x's number of elements")
+    _check(lib().fp8_cast_amax(_ptr(x), x.numel(), _ptr(scale), int(fmt), _ptr(out), _ptr(scale_inv_out),
+                               _ptr(amax_slot), _ptr(noop), _stream(stream)))
+
+
+def fp8_cast_transpose(x, scale, fmt, out, out_t, scale_inv_out=None, amax_slot=None, noop=None, stream=None):
+    """Cast a 2-D bfloat16 ``x`` [R, C] to ``out`` [R, C] and its transpose ``out_t`` [C, R]."""
+    _want(x, _BF16, "x")
+    _want(out, (torch.uint8,), "out")
+    _want(out_t, (torch.uint8,), "out_t")
+    R, C = x.shape
+    if tuple(out.shape) != (R, C) or tuple(out_t.shape) != (C, R):
+        raise ValueError("out must be [R, C] and out_t [C, R]")
+    _check(lib().fp8_cast_transpose(_ptr(x), R, C, _ptr(scale), int(fmt), _ptr(out), _ptr(out_t),
+                                    _ptr(scale_inv_out), _ptr(amax_slot), _ptr(noop), _stream(stream)))
+
+
+def fp8_dbias_workspace_bytes(rows: int, cols: int) -> int:
+    return int(lib().fp8_dbias_workspace_bytes(int(rows), int(cols)))
+
+
+def fp8_dbias_cast_transpose(dy, scale, fmt, out, out_t, dbias, workspace, scale_inv_out=None, amax_slot=None,
+                             stream=None):
+    """dbias = column sums of ``dy`` plus its cast+transpose (see include/fp8ds.h)."""
+    _want(dy, _BF16, "dy")
+    _want(dbias, (torch.float32,), "dbias")
+    R, C = dy.shape
+    if out is not None and (tuple(out.shape) != (R, C) or tuple(out_t.shape) != (C, R)):
+        raise ValueError("out must be [R, C] and out_t [C, R]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fp8_dbias_cast_transpose(_ptr(dy), R, C, _ptr(scale), int(fmt), _ptr(out), _ptr(out_t),
+                                          _ptr(scale_inv_out), _ptr(amax_slot), _ptr(dbias), _ptr(workspace),
+                                          ws_bytes, _stream(stream)))
+
+
+def fp8_scale_update(amax_history, scale, scale_inv, fmts: Sequence[int], margin: int = 0, stream=None):
+    """One delayed-scaling step for the T tensors of ``amax_history`` [L, T]."""
+    _want(amax_history, (torch.float32,), "amax_history")
+    L, T = amax_history.shape
+    f = (ctypes.c_int32 * T)(*[int(v) for v in fmts])
+    if len(fmts) != T:
+        raise ValueError("one format per tensor")
+    _check(lib().fp8_scale_update(_ptr(amax_history), L, T, _ptr(scale), _ptr(scale_inv),
+                                  ctypes.cast(f, ctypes.c_void_p), int(margin), _stream(stream)))
+
+
+def _out_dtype(D):
+    if D.dtype == torch.bfloat16:
+        return OUT_BF16
+    if D.dtype == torch.float32:
+        return OUT_FP32
+    raise TypeError("D must be bfloat16 or float32")
+
+
+def _gemm_args(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D):
+    _want(A, (torch.uint8,), "A", contiguous=False)
+    _want(B, (torch.uint8,), "B", contiguous=False)
+    _want(bias, _BF16, "bias")
+    M, K = A.shape
+    N, K2 = B.shape
+    if K != K2:
+        raise ValueError("A and B must share K")
+    if tuple(D.shape) != (M, N):
+        raise ValueError("D must be [M, N]")
+    for t, nm in ((A, "A"), (B, "B"), (D, "D")):
+        if t.stride(1) != 1:
+            raise ValueError(f"{nm} rows must be contiguous")
+    return (_ptr(A), int(fa), _ptr(a_scale_inv), A.stride(0), _ptr(B), int(fb), _ptr(b_scale_inv), B.stride(0),
+            _ptr(bias), _ptr(D), D.stride(0), _out_dtype(D), M, N, K)
+
+
+def fp8_gemm_bias(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D, stream=None):
+    """D = (A B^T) * a_scale_inv * b_scale_inv + bias, A [M, K] and B [N, K] FP8 codes."""
+    _check(lib().fp8_gemm_bias(*_gemm_args(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D), _stream(stream)))
+
+
+def fp8_gemm_bias_chunked(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D, n_chunks: int,
+                          chunk_streams=None, stream=None):
+    """The N-chunked GEMM: chunk c on ``chunk_streams[c]`` with its own bias offset."""
+    arr = None
+    if chunk_streams is not None:
+        if len(chunk_streams) < n_chunks:
+            raise ValueError("one stream per chunk")
+        arr = (ctypes.c_void_p * n_chunks)(*[_stream(s) for s in chunk_streams[:n_chunks]])
+    _check(lib().fp8_gemm_bias_chunked(*_gemm_args(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D),
+                                       int(n_chunks), None if arr is None else ctypes.cast(arr, ctypes.c_void_p),
+                                       _stream(stream)))
+
+
+def fp8_linear_fwd(x, w, bias, x_scale, x_amax, x8, x8_t, x_scale_inv, w_scale, w_amax, w8, w8_t, w_scale_inv,
+                   w_noop, y, stream=None):
+    """Forward of the FP8 linear layer: casts of x and W, then y = x8 W8^T + bias."""
+    _want(x, _BF16, "x")
+    _want(w, _BF16, "w")
+    _want(y, (torch.bfloat16,), "y")
+    M, K = x.shape
+    N, K2 = w.shape
+    if K != K2 or tuple(y.shape) != (M, N):
+        raise ValueError("x [M, K], w [N, K], y [M, N]")
+    _check(lib().fp8_linear_fwd(_ptr(x), _ptr(w), _ptr(bias), M, N, K, _ptr(x_scale), _ptr(x_amax), _ptr(x8),
+                                _ptr(x8_t), _ptr(x_scale_inv), _ptr(w_scale), _ptr(w_amax), _ptr(w8), _ptr(w8_t),
+                                _ptr(w_scale_inv), _ptr(w_noop), _ptr(y), _stream(stream)))
+
+
+def fp8_linear_bwd(dy, K, dy_scale, dy_amax, dy8, dy8_t, dy_scale_inv, dbias, workspace, x8_t, x_scale_inv, w8_t,
+                   w_scale_inv, dx, dw, stream=None):
+    """Backward of the FP8 linear layer: dbias + cast+transpose of dy, dgrad and wgrad GEMMs."""
+    _want(dy, _BF16, "dy")
+    M, N = dy.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fp8_linear_bwd(_ptr(dy), M, N, int(K), _ptr(dy_scale), _ptr(dy_amax), _ptr(dy8), _ptr(dy8_t),
+                                _ptr(dy_scale_inv), _ptr(dbias), _ptr(workspace), ws_bytes, _ptr(x8_t),
+                                _ptr(x_scale_inv), _ptr(w8_t), _ptr(w_scale_inv), _ptr(dx), _ptr(dw),
+                                _out_dtype(dw), _stream(stream)))

@@ -1,0 +1,358 @@
+// cast.hip -- the cast family of the FP8 delayed-scaling path on gfx950:
+//   cast + amax                  (Float8Tensor.to_float8 in "[PyTorch] cuda graph support",
+//                                 transpose-cache thread)
+//   cast + transpose + amax      (the transpose cache of "[PyTorch] Refactor FP8 workspaces in
+//                                 linear modules", "grown in scope" first bullet)
+//   dbias + cast + transpose     (DbiasCastTranspose in "[PyTorch] cuda graph support")
+//
+// All three are HBM-streaming kernels.  Reads are 16-byte per lane and coalesced along rows;
+// the FP8 codes are produced by the hardware converter after a v_med3 clamp (saturation);
+// the transposed copy is built by converting column pairs straight into packed dwords and
+// exchanging 8-byte fragments through LDS, so both outputs leave in coalesced stores.
+// The amax is a packed 16-bit integer max of the bfloat16 magnitudes, reduced per wave and
+// per block, with one atomic per block.
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8ds {
+
+// ------------------------------------------------------------------------------------------
+// 1-D cast + amax.  Each thread converts 16 elements per step (two 16-byte loads, one 16-byte
+// store) in a grid-stride loop; the tail (numel % 16) is converted element by element.
+// ------------------------------------------------------------------------------------------
+template <int FMT>
+__global__ __launch_bounds__(256) void k_cast_amax(const uint16_t *__restrict__ x, int64_t n,
+                                                   const float *__restrict__ scale_p,
+                                                   uint8_t *__restrict__ out,
+                                                   float *__restrict__ sinv_out, float *amax_slot,
+                                                   const float *__restrict__ noop) {
+    __shared__ uint32_t red[4];
+    if (noop != nullptr && *noop == 1.0f) return;
+    const float s = *scale_p;
+    const bool plain = scale_is_plain(s);
+    uint32_t am = 0;
+    const int64_t nvec = n >> 4;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (v << 4));
+        u32x4 p = __builtin_nontemporal_load(src);
+        u32x4 q = __builtin_nontemporal_load(src + 1);
+        uint32_t w[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+        uint32_t tam = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tam = amax_pk(tam, w[i]);
+        uint32_t o[4];
+        if (plain && amax_unpack(tam) < 0x7F80u) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                o[i] = pack4<FMT>(clamp_fmt<FMT>(bf16_lo(w[2 * i]) * s), clamp_fmt<FMT>(bf16_hi(w[2 * i]) * s),
+                                  clamp_fmt<FMT>(bf16_lo(w[2 * i + 1]) * s),
+                                  clamp_fmt<FMT>(bf16_hi(w[2 * i + 1]) * s));
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                o[i] = encode_exact<FMT>(bf16_lo(w[2 * i]) * s) | (encode_exact<FMT>(bf16_hi(w[2 * i]) * s) << 8) |
+                       (encode_exact<FMT>(bf16_lo(w[2 * i + 1]) * s) << 16) |
+                       (encode_exact<FMT>(bf16_hi(w[2 * i + 1]) * s) << 24);
+        }
+        am = amax_pk(am, tam);
+        u32x4 ov = {o[0], o[1], o[2], o[3]};
+        __builtin_nontemporal_store(ov, reinterpret_cast<u32x4 *>(out + (v << 4)));
+    }
+    // tail
+    for (int64_t i = (nvec << 4) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        uint32_t w = x[i];
+        am = amax_pk(am, w);
+        out[i] = (uint8_t)encode_exact<FMT>(bf16_lo(w) * s);
+    }
+    uint32_t bm = block_max_u32<256>(amax_unpack(am), red);
+    if (threadIdx.x == 0) {
+        fold_amax(amax_slot, bm);
+        if (blockIdx.x == 0 && sinv_out != nullptr) *sinv_out = 1.0f / s;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// 2-D cast + transpose (+ dbias partials).  A 256-thread block owns a 128 x 128 tile; thread
+// (rb = t / 16, cb = t % 16) owns the 8 x 8 micro-tile at rows 8rb.., columns 8cb...
+//   loads   : eight 16-byte row segments (one per micro-tile row);
+//   out     : per row, four codes from column pairs -> 8-byte store (16 lanes = 128 B per row);
+//   out_t   : per column, row pairs converted straight into dwords -> 8-byte fragment into
+//             LDS tile T[col][row] -> after a barrier each thread stores 16-byte row chunks
+//             of the transposed tile (8 lanes = 128 B per transposed row);
+//   dbias   : per-column sums of the micro-tile, reduced over the 16 row blocks through LDS in
+//             a fixed order, one partial per (row tile, column) into the workspace.
+// VEC: cols % 8 == 0 and rows % 16 == 0, so every 16-byte load, 8-byte store and 16-byte
+// transposed store is either wholly inside the tensor or wholly outside.  Otherwise each element
+// is loaded and stored on its own with bounds checks (same tile structure).
+// ------------------------------------------------------------------------------------------
+constexpr int kTile = 128;
+// The transposed tile lives in LDS as T[col][row] (128 x 128 bytes, no padding).  The 8-byte
+// fragment of row block rb in transposed row `col` sits at slot rb ^ ((col >> 3) & 15): the 16
+// lanes that write one row block all hit different 8-byte slots, and a 16-byte read of chunk p
+// finds its two halves at slots 2p ^ g and (2p + 1) ^ g, i.e. in 16-byte chunk p ^ (g >> 1),
+// swapped when g is odd.
+__device__ __forceinline__ int t_swz(int col) { return (col >> 3) & 15; }
+
+template <int FMT, bool VEC, bool DBIAS>
+__global__ __launch_bounds__(256) void k_cast_transpose(const uint16_t *__restrict__ x, int64_t rows,
+                                                        int64_t cols, const float *__restrict__ scale_p,
+                                                        uint8_t *__restrict__ out, uint8_t *__restrict__ out_t,
+                                                        float *__restrict__ sinv_out, float *amax_slot,
+                                                        const float *__restrict__ noop,
+                                                        float *__restrict__ partial) {
+    __shared__ __align__(16) uint8_t tT[kTile * kTile];
+    __shared__ float csum[DBIAS ? 16 * kTile : 1];
+    __shared__ uint32_t red[4];
+    if (noop != nullptr && *noop == 1.0f) return;
+
+    const float s = *scale_p;
+    const int t = threadIdx.x;
+    const int rb = t >> 4, cb = t & 15;
+    const int64_t tiles_c = (cols + kTile - 1) / kTile;
+    const int64_t tile_r = blockIdx.x / tiles_c, tile_c = blockIdx.x - tile_r * tiles_c;
+    const int64_t r0 = tile_r * kTile;
+    const int64_t c0 = tile_c * kTile;
+    const int64_t row = r0 + rb * 8;   // first row of the micro-tile
+    const int64_t col = c0 + cb * 8;   // first column of the micro-tile
+
+    // ---- load 8 rows x 8 columns (bfloat16 pairs in dwords: w[r][0..3])
+    uint32_t w[8][4];
+    if constexpr (VEC) {
+        const bool cin = col < cols;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            if (cin && row + r < rows) {
+                u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + (row + r) * cols + col));
+                w[r][0] = v.x; w[r][1] = v.y; w[r][2] = v.z; w[r][3] = v.w;
+            } else {
+                w[r][0] = w[r][1] = w[r][2] = w[r][3] = 0u;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                uint32_t lo = 0, hi = 0;
+                if (row + r < rows) {
+                    if (col + 2 * c < cols) lo = x[(row + r) * cols + col + 2 * c];
+                    if (col + 2 * c + 1 < cols) hi = x[(row + r) * cols + col + 2 * c + 1];
+                }
+                w[r][c] = lo | (hi << 16);
+            }
+        }
+    }
+
+    // ---- amax of the micro-tile (out-of-range elements are zero)
+    uint32_t tam = 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) tam = amax_pk(tam, w[r][c]);
+    const uint32_t mag = amax_unpack(tam);
+
+    // ---- dbias: column sums of the micro-tile in row order
+    if constexpr (DBIAS) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float slo = 0.f, shi = 0.f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                slo += bf16_lo(w[r][c]);
+                shi += bf16_hi(w[r][c]);
+            }
+            csum[rb * kTile + cb * 8 + 2 * c] = slo;
+            csum[rb * kTile + cb * 8 + 2 * c + 1] = shi;
+        }
+    }
+
+    // ---- scaled, clamped values y[r][c]
+    uint32_t orow[8][2];   // row-major codes: row r, columns 0-3 / 4-7
+    uint32_t ocol[8][2];   // transposed codes: column c, rows 0-3 / 4-7
+    if (scale_is_plain(s) && mag < 0x7F80u) {
+        float y[8][8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                y[r][2 * c] = clamp_fmt<FMT>(bf16_lo(w[r][c]) * s);
+                y[r][2 * c + 1] = clamp_fmt<FMT>(bf16_hi(w[r][c]) * s);
+            }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            orow[r][0] = pack4<FMT>(y[r][0], y[r][1], y[r][2], y[r][3]);
+            orow[r][1] = pack4<FMT>(y[r][4], y[r][5], y[r][6], y[r][7]);
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            ocol[c][0] = pack4<FMT>(y[0][c], y[1][c], y[2][c], y[3][c]);
+            ocol[c][1] = pack4<FMT>(y[4][c], y[5][c], y[6][c], y[7][c]);
+        }
+    } else {
+        uint32_t e[8][8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                e[r][2 * c] = encode_exact<FMT>(bf16_lo(w[r][c]) * s);
+                e[r][2 * c + 1] = encode_exact<FMT>(bf16_hi(w[r][c]) * s);
+            }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            orow[r][0] = e[r][0] | (e[r][1] << 8) | (e[r][2] << 16) | (e[r][3] << 24);
+            orow[r][1] = e[r][4] | (e[r][5] << 8) | (e[r][6] << 16) | (e[r][7] << 24);
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            ocol[c][0] = e[0][c] | (e[1][c] << 8) | (e[2][c] << 16) | (e[3][c] << 24);
+            ocol[c][1] = e[4][c] | (e[5][c] << 8) | (e[6][c] << 16) | (e[7][c] << 24);
+        }
+    }
+
+    // ---- transposed fragments into LDS: T[cb*8 + c][rb*8 .. rb*8+7]
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int tc = cb * 8 + c;
+        u32x2 v = {ocol[c][0], ocol[c][1]};
+        *reinterpret_cast<u32x2 *>(&tT[tc * kTile + ((rb ^ t_swz(tc)) << 3)]) = v;
+    }
+
+    // ---- row-major codes straight to global memory
+    if constexpr (VEC) {
+        if (col < cols) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                if (row + r < rows)
+                {
+                    u32x2 v = {orow[r][0], orow[r][1]};
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(out + (row + r) * cols + col));
+                }
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                if (row + r < rows && col + c < cols)
+                    out[(row + r) * cols + col + c] = (uint8_t)(orow[r][c >> 2] >> (8 * (c & 3)));
+    }
+
+    __syncthreads();
+
+    // ---- transposed tile out: 128 transposed rows x 128 bytes, 16-byte chunks
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = t + 256 * i;
+        const int tr = q >> 3, part = q & 7;          // transposed row (= tile column), chunk
+        const int64_t orow_g = c0 + tr;                 // row of out_t
+        const int64_t ocol_g = r0 + part * 16;          // first column of out_t in this chunk
+        const int g = t_swz(tr);
+        u32x4 v = *reinterpret_cast<const u32x4 *>(&tT[tr * kTile + ((part ^ (g >> 1)) << 4)]);
+        if (g & 1) v = v.zwxy;
+        if constexpr (VEC) {
+            if (orow_g < cols && ocol_g < rows)
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(out_t + orow_g * rows + ocol_g));
+        } else {
+            if (orow_g < cols) {
+                const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int b = 0; b < 16; ++b)
+                    if (ocol_g + b < rows) out_t[orow_g * rows + ocol_g + b] = (uint8_t)(d[b >> 2] >> (8 * (b & 3)));
+            }
+        }
+    }
+
+    // ---- dbias partial of this row tile: fixed-order sum over the 16 row blocks
+    if constexpr (DBIAS) {
+        if (t < kTile) {
+            float acc = 0.f;
+#pragma unroll
+            for (int b = 0; b < 16; ++b) acc += csum[b * kTile + t];
+            if (c0 + t < cols) partial[tile_r * cols + c0 + t] = acc;
+        }
+    }
+
+    // ---- amax: one atomic per block; inverse scale from block (0, 0)
+    uint32_t bm = block_max_u32<256>(mag, red);
+    if (t == 0) {
+        fold_amax(amax_slot, bm);
+        if (blockIdx.x == 0 && sinv_out != nullptr) *sinv_out = 1.0f / s;
+    }
+}
+
+// dbias[j] = sum over row tiles (in order) of partial[tile][j].
+__global__ __launch_bounds__(256) void k_dbias_reduce(const float *__restrict__ partial, int64_t ntiles,
+                                                      int64_t cols, float *__restrict__ dbias) {
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= cols) return;
+    float acc = 0.f;
+    for (int64_t i = 0; i < ntiles; ++i) acc += partial[i * cols + j];
+    dbias[j] = acc;
+}
+
+// ------------------------------------------------------------------------------------------
+// launchers
+// ------------------------------------------------------------------------------------------
+hipError_t launch_cast_amax(const uint16_t *x, int64_t n, const float *scale, int fmt, uint8_t *out,
+                            float *sinv_out, float *amax_slot, const float *noop, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    int64_t nvec = n >> 4;
+    int64_t blocks = (nvec + 255) / 256;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 256 * 16) blocks = 256 * 16;  // grid-stride beyond 16 blocks per CU
+    if (fmt == kE4M3)
+        k_cast_amax<kE4M3><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(x, n, scale, out, sinv_out, amax_slot, noop);
+    else
+        k_cast_amax<kE5M2><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(x, n, scale, out, sinv_out, amax_slot, noop);
+    return hipGetLastError();
+}
+
+template <bool DBIAS>
+static hipError_t launch_ct(const uint16_t *x, int64_t rows, int64_t cols, const float *scale, int fmt,
+                            uint8_t *out, uint8_t *out_t, float *sinv_out, float *amax_slot,
+                            const float *noop, float *partial, hipStream_t st) {
+    dim3 grid((unsigned)(((cols + kTile - 1) / kTile) * ((rows + kTile - 1) / kTile)));
+    const bool vec = (cols % 8 == 0) && (rows % 16 == 0);
+#define FP8DS_CT(F, V) \
+    k_cast_transpose<F, V, DBIAS><<<grid, dim3(256), 0, st>>>(x, rows, cols, scale, out, out_t, sinv_out, amax_slot, noop, partial)
+    if (fmt == kE4M3) {
+        if (vec) FP8DS_CT(kE4M3, true); else FP8DS_CT(kE4M3, false);
+    } else {
+        if (vec) FP8DS_CT(kE5M2, true); else FP8DS_CT(kE5M2, false);
+    }
+#undef FP8DS_CT
+    return hipGetLastError();
+}
+
+hipError_t launch_cast_transpose(const uint16_t *x, int64_t rows, int64_t cols, const float *scale, int fmt,
+                                 uint8_t *out, uint8_t *out_t, float *sinv_out, float *amax_slot,
+                                 const float *noop, hipStream_t st) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    return launch_ct<false>(x, rows, cols, scale, fmt, out, out_t, sinv_out, amax_slot, noop, nullptr, st);
+}
+
+size_t dbias_workspace_bytes(int64_t rows, int64_t cols) {
+    if (rows <= 0 || cols <= 0) return 0;
+    return (size_t)((rows + kTile - 1) / kTile) * (size_t)cols * sizeof(float);
+}
+
+hipError_t launch_dbias_cast_transpose(const uint16_t *dy, int64_t rows, int64_t cols, const float *scale,
+                                       int fmt, uint8_t *out, uint8_t *out_t, float *sinv_out,
+                                       float *amax_slot, float *dbias, void *ws, hipStream_t st) {
+    if (cols == 0) return hipSuccess;
+    if (rows == 0) {
+        // no rows: the column sums are zero; nothing else to write (a fill kernel, not a
+        // memset node, so the call stays safe to capture into a graph)
+        k_dbias_reduce<<<dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, st>>>(nullptr, 0, cols, dbias);
+        return hipGetLastError();
+    }
+    float *partial = static_cast<float *>(ws);
+    hipError_t e = launch_ct<true>(dy, rows, cols, scale, fmt, out, out_t, sinv_out, amax_slot, nullptr, partial, st);
+    if (e != hipSuccess) return e;
+    const int64_t ntiles = (rows + kTile - 1) / kTile;
+    k_dbias_reduce<<<dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, st>>>(partial, ntiles, cols, dbias);
+    return hipGetLastError();
+}
+
+}  // namespace fp8ds

@@ -1,0 +1,246 @@
+// gemm.hip -- FP8 GEMM with inverse-scale dequantisation and bias on gfx950 matrix cores.
+//
+//   D[m, n] = (sum_k A[m, k] * B[n, k]) * a_scale_inv * b_scale_inv + bias[n]
+//
+// The fp8_gemm of "[PyTorch] cuda graph support" (transpose-cache thread, FP8Linear.backward)
+// and the per-chunk bias of "[PyTorch] Userbuffers support in operation-based API" (bias-offset
+// fix).  Both operands are K-contiguous ("TN"); the transposes the backward needs come from
+// the cast+transpose kernels, so the GEMM never transposes.
+//
+// Design (CDNA4):
+//   * block tile 256 x 256, K step 128 bytes, 256 threads = 4 waves in a 2 x 2 grid, each wave
+//     a 128 x 128 sub-tile made of 4 x 4 v_mfma_f32_32x32x64_f8f6f4 tiles (float32 accumulate;
+//     the A / B formats are the instruction's cbsz / blgp selectors, so E4M3 x E4M3,
+//     E5M2 x E4M3 and the others share one kernel template);
+//   * global -> registers -> LDS, double-buffered LDS (2 x 64 KB of the 160 KB), one barrier per
+//     K step, the next K step's global loads in flight during the current step's MFMAs;
+//   * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
+//     c ^ (r & 7) ^ ((r >> 3) & 1), so the 32 rows one MFMA operand read touches spread over
+//     all banks;
+//   * blocks are remapped so that each XCD (blocks are dealt round-robin to the 8 XCDs) works
+//     on a contiguous range of tiles, walked in groups of 8 tile-rows for L2 reuse;
+//   * epilogue: acc * a_scale_inv * b_scale_inv + bias in float32, rounded to bfloat16 (nearest
+//     even) or stored as float32.
+// Ragged M / N are handled by clamping the rows that are loaded and masking the stores; a
+// ragged K (a multiple of 16) by zero-filling the 16-byte chunks past K.  No split-K: every
+// output element is one fixed sequence of MFMAs over K, whatever tile it falls in.
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8ds {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+namespace {
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int kThreads = 256;
+constexpr int kGroupM = 8;
+constexpr int kLdsA = BM * BK;             // bytes per A buffer
+constexpr int kLdsB = BN * BK;
+constexpr int kLdsBytes = 2 * (kLdsA + kLdsB);
+
+__device__ __forceinline__ int lds_chunk(int row, int c) { return c ^ (row & 7) ^ ((row >> 3) & 1); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
+    uint32_t u = __float_as_uint(v);
+    if (v != v) return 0x7FC0u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+}  // namespace
+
+template <int FA, int FB, int OUT>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_bias(const uint8_t *__restrict__ A, int64_t lda,
+                                                           const uint8_t *__restrict__ B, int64_t ldb,
+                                                           const float *__restrict__ a_sinv,
+                                                           const float *__restrict__ b_sinv,
+                                                           const uint16_t *__restrict__ bias,
+                                                           void *__restrict__ D, int64_t ldd, int M, int N,
+                                                           int K, int tiles_m, int tiles_n) {
+    __shared__ __align__(16) uint8_t smem[kLdsBytes];
+
+    // ---- tile of this block: XCD-contiguous ranges, grouped row-major walk
+    const int nwg = tiles_m * tiles_n;
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, local = bid >> 3;
+    const int q8 = nwg >> 3, r8 = nwg & 7;
+    const int tile = (xcd < r8) ? xcd * (q8 + 1) + local : r8 * (q8 + 1) + (xcd - r8) * q8 + local;
+    const int group = tile / (kGroupM * tiles_n);
+    const int first_m = group * kGroupM;
+    const int gm = min(tiles_m - first_m, kGroupM);
+    const int in_group = tile - group * kGroupM * tiles_n;
+    const int tm = first_m + in_group % gm;
+    const int tn = in_group / gm;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // ---- global load assignment: 8 chunks of 16 bytes per operand per K step
+    //      chunk i: tile row (tid >> 3) + 32 i, 16-byte column part (tid & 7)
+    const int lrow = tid >> 3, part = tid & 7;
+    const uint8_t *pa[8];
+    const uint8_t *pb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int ra = min(m0 + lrow + 32 * i, M - 1);
+        const int rb = min(n0 + lrow + 32 * i, N - 1);
+        pa[i] = A + (int64_t)ra * lda + part * 16;
+        pb[i] = B + (int64_t)rb * ldb + part * 16;
+    }
+    int lds_off[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = lrow + 32 * i;
+        lds_off[i] = r * BK + lds_chunk(r, part) * 16;
+    }
+
+    u32x4 ra_[8], rb_[8];
+    auto gload = [&](int kt) {
+        const int kofs = kt * BK;
+        const bool ok = kofs + part * 16 < K;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (ok) {
+                ra_[i] = *reinterpret_cast<const u32x4 *>(pa[i] + kofs);
+                rb_[i] = *reinterpret_cast<const u32x4 *>(pb[i] + kofs);
+            } else {
+                ra_[i] = u32x4{0u, 0u, 0u, 0u};
+                rb_[i] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto lstore = [&](int buf) {
+        uint8_t *as = smem + buf * kLdsA;
+        uint8_t *bs = smem + 2 * kLdsA + buf * kLdsB;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            *reinterpret_cast<u32x4 *>(as + lds_off[i]) = ra_[i];
+            *reinterpret_cast<u32x4 *>(bs + lds_off[i]) = rb_[i];
+        }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    // operand read positions: lane supplies row (lane & 31) of a 32-row MFMA tile and the 32
+    // bytes [32 * (lane >> 5), +32) of each 64-byte K sub-step (the same K bytes for A and B,
+    // so the K order inside the instruction is the same on both sides)
+    const int frow = lane & 31, fhalf = lane >> 5;
+    auto frag = [&](const uint8_t *base, int row, int ks) -> i32x8 {
+        const int c0 = ks * 4 + fhalf * 2;
+        u32x4 lo = *reinterpret_cast<const u32x4 *>(base + row * BK + lds_chunk(row, c0) * 16);
+        u32x4 hi = *reinterpret_cast<const u32x4 *>(base + row * BK + lds_chunk(row, c0 + 1) * 16);
+        i32x8 r;
+        r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+        r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+        return r;
+    };
+
+    const int nk = (K + BK - 1) / BK;
+    if (nk > 0) {
+        gload(0);
+        lstore(0);
+        __syncthreads();
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) gload(kt + 1);
+        const uint8_t *as = smem + buf * kLdsA;
+        const uint8_t *bs = smem + 2 * kLdsA + buf * kLdsB;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            i32x8 af[4], bf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                af[i] = frag(as, wm * 128 + i * 32 + frow, ks);
+                bf[i] = frag(bs, wn * 128 + i * 32 + frow, ks);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], FA, FB,
+                                                                                 0, 0, 0, 0);
+        }
+        if (kt + 1 < nk) lstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue.  Accumulator element e of lane l in a 32 x 32 tile is row
+    //      (e / 4) * 8 + (l / 32) * 4 + e % 4, column l % 32.
+    const float sa = *a_sinv, sb = *b_sinv;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int col = n0 + wn * 128 + j * 32 + frow;
+        if (col >= N) continue;
+        const float bv = bias != nullptr ? __uint_as_float((uint32_t)bias[col] << 16) : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = m0 + wm * 128 + i * 32 + (e >> 2) * 8 + fhalf * 4 + (e & 3);
+                if (row < M) {
+                    const float v = acc[i][j][e] * sa * sb + bv;
+                    if constexpr (OUT == 0)
+                        reinterpret_cast<uint16_t *>(D)[(int64_t)row * ldd + col] = f32_to_bf16_rne(v);
+                    else
+                        reinterpret_cast<float *>(D)[(int64_t)row * ldd + col] = v;
+                }
+            }
+        }
+    }
+}
+
+// D = bias broadcast (K == 0): no products at all.
+template <int OUT>
+__global__ __launch_bounds__(256) void k_bias_only(const uint16_t *__restrict__ bias, void *__restrict__ D,
+                                                   int64_t ldd, int M, int N) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)M * N) return;
+    const int64_t m = idx / N, n = idx % N;
+    const float v = bias != nullptr ? __uint_as_float((uint32_t)bias[n] << 16) : 0.f;
+    if constexpr (OUT == 0)
+        reinterpret_cast<uint16_t *>(D)[m * ldd + n] = f32_to_bf16_rne(v);
+    else
+        reinterpret_cast<float *>(D)[m * ldd + n] = v;
+}
+
+hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64_t lda, const uint8_t *B, int fb,
+                            const float *b_sinv, int64_t ldb, const uint16_t *bias, void *D, int64_t ldd,
+                            int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+    if (M == 0 || N == 0) return hipSuccess;
+    if (K == 0) {
+        const int64_t total = M * N;
+        dim3 grid((unsigned)((total + 255) / 256));
+        if (out_dtype == 0) k_bias_only<0><<<grid, 256, 0, st>>>(bias, D, ldd, (int)M, (int)N);
+        else k_bias_only<1><<<grid, 256, 0, st>>>(bias, D, ldd, (int)M, (int)N);
+        return hipGetLastError();
+    }
+    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+    dim3 grid((unsigned)(tiles_m * tiles_n));
+#define FP8DS_GEMM(FA_, FB_, O_)                                                                           \
+    k_gemm_bias<FA_, FB_, O_><<<grid, dim3(kThreads), 0, st>>>(A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, \
+                                                               (int)M, (int)N, (int)K, tiles_m, tiles_n)
+    const int sel = fa * 4 + fb * 2 + out_dtype;
+    switch (sel) {
+        case 0: FP8DS_GEMM(kE4M3, kE4M3, 0); break;
+        case 1: FP8DS_GEMM(kE4M3, kE4M3, 1); break;
+        case 2: FP8DS_GEMM(kE4M3, kE5M2, 0); break;
+        case 3: FP8DS_GEMM(kE4M3, kE5M2, 1); break;
+        case 4: FP8DS_GEMM(kE5M2, kE4M3, 0); break;
+        case 5: FP8DS_GEMM(kE5M2, kE4M3, 1); break;
+        case 6: FP8DS_GEMM(kE5M2, kE5M2, 0); break;
+        default: FP8DS_GEMM(kE5M2, kE5M2, 1); break;
+    }
+#undef FP8DS_GEMM
+    return hipGetLastError();
+}
+
+}  // namespace fp8ds

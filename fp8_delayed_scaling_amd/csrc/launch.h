@@ -1,0 +1,28 @@
+// launch.h -- internal launchers behind the C ABI (host side; arguments already validated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8ds {
+
+hipError_t launch_cast_amax(const uint16_t *x, int64_t n, const float *scale, int fmt, uint8_t *out,
+                            float *sinv_out, float *amax_slot, const float *noop, hipStream_t st);
+hipError_t launch_cast_transpose(const uint16_t *x, int64_t rows, int64_t cols, const float *scale, int fmt,
+                                 uint8_t *out, uint8_t *out_t, float *sinv_out, float *amax_slot,
+                                 const float *noop, hipStream_t st);
+size_t dbias_workspace_bytes(int64_t rows, int64_t cols);
+hipError_t launch_dbias_cast_transpose(const uint16_t *dy, int64_t rows, int64_t cols, const float *scale,
+                                       int fmt, uint8_t *out, uint8_t *out_t, float *sinv_out,
+                                       float *amax_slot, float *dbias, void *ws, hipStream_t st);
+
+constexpr int kMaxScaleTensors = 4096;
+hipError_t launch_scale_update(float *hist, int64_t L, int64_t T, float *scale, float *scale_inv,
+                               const int32_t *fmts_host, int32_t margin, hipStream_t st);
+
+hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64_t lda, const uint8_t *B, int fb,
+                            const float *b_sinv, int64_t ldb, const uint16_t *bias, void *D, int64_t ldd,
+                            int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t st);
+
+}  // namespace fp8ds

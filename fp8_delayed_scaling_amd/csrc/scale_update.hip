@@ -1,0 +1,83 @@
+// scale_update.hip -- fused delayed-scaling update of T tensors in one launch: history max,
+// guarded scale recompute and history roll.  The scale-update kernel, and a fix for amaxes small
+// enough to drive the scale to infinity, are named in "[PyTorch] Refactor FP8 workspaces in
+// linear modules" (Motivations, first bullet); amaxes are reduced within the current iteration
+// ("[PyTorch] cuda graph support", feature list).
+//
+// One 256-thread block per tensor.  The history is [L][T] float32 (row 0 = current amaxes), so
+// a tensor's column is strided by T; at the sizes this runs at (L up to a few thousand, T up to
+// a few thousand) the kernel is launch-latency bound, not bandwidth bound.
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8ds {
+
+struct FmtMask {
+    uint32_t bits[kMaxScaleTensors / 32];  // bit t set: tensor t is E5M2, else E4M3
+};
+
+__global__ __launch_bounds__(256) void k_scale_update(float *__restrict__ hist, int64_t L, int64_t T,
+                                                      float *__restrict__ scale, float *__restrict__ scale_inv,
+                                                      FmtMask fm, float pow2_neg_margin) {
+    __shared__ float red[4];
+    __shared__ int nanflag;
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (tid == 0) nanflag = 0;
+    __syncthreads();
+
+    // pass 1: max over the window (all L rows), NaN tracked on its own
+    float a = 0.f;
+    bool nan = false;
+    for (int64_t i = tid; i < L; i += 256) {
+        const float h = hist[i * T + t];
+        nan |= (h != h);
+        a = fmaxf(a, h);
+    }
+    if (nan) nanflag = 1;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+    if ((tid & 63) == 0) red[tid >> 6] = a;
+    const float row0 = hist[t];   // old row 0, read before any write below
+    __syncthreads();
+
+    if (tid == 0) {
+        float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        if (nanflag) amax = __uint_as_float(0x7FC00000u);
+        const bool e5 = (fm.bits[t >> 5] >> (t & 31)) & 1u;
+        const float fmax = e5 ? FmtTraits<kE5M2>::kMax : FmtTraits<kE4M3>::kMax;
+        float s = (fmax / amax) * pow2_neg_margin;
+        const bool bad = !(amax > 0.f) || !(amax < __uint_as_float(0x7F800000u)) ||
+                         !(fabsf(s) < __uint_as_float(0x7F800000u)) || s == 0.f;
+        if (bad) s = scale[t];
+        scale[t] = s;
+        scale_inv[t] = 1.0f / s;
+    }
+
+    // pass 2: roll towards row 0 in chunks of 256 rows (read row i+1, barrier, write row i)
+    for (int64_t base = 0; base < L - 1; base += 256) {
+        const int64_t i = base + tid;
+        float v = 0.f;
+        if (i < L - 1) v = hist[(i + 1) * T + t];
+        __syncthreads();
+        if (i < L - 1) hist[i * T + t] = v;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        hist[(L - 1) * T + t] = row0;   // the amax just used becomes the newest past entry
+        hist[t] = 0.f;                  // row 0 cleared for the next iteration
+    }
+}
+
+hipError_t launch_scale_update(float *hist, int64_t L, int64_t T, float *scale, float *scale_inv,
+                               const int32_t *fmts_host, int32_t margin, hipStream_t st) {
+    FmtMask fm;
+    for (int i = 0; i < kMaxScaleTensors / 32; ++i) fm.bits[i] = 0u;
+    for (int64_t t = 0; t < T; ++t)
+        if (fmts_host[t] == kE5M2) fm.bits[t >> 5] |= 1u << (t & 31);
+    const float p = ldexpf(1.0f, -margin);   // exact power of two for |margin| <= 126
+    k_scale_update<<<dim3((unsigned)T), dim3(256), 0, st>>>(hist, L, T, scale, scale_inv, fm, p);
+    return hipGetLastError();
+}
+
+}  // namespace fp8ds

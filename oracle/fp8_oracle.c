@@ -66,7 +66,9 @@ static int fmt_emin(int fmt) { return 1 - fmt_bias(fmt); }
 
 /*
  * Encode a float32 into FP8, saturating, round-to-nearest-even.
- *   NaN              -> 0x7F with the input's sign bit (the NaN code of both formats);
+ *   NaN              -> 0x7F, the positive all-ones NaN code of both formats, whatever the
+ *                       NaN's sign bit (IEEE 754 leaves the sign of a NaN made by an invalid
+ *                       operation such as inf * 0 unspecified, so it carries no information);
  *   |f| > max finite -> the largest finite code with the input's sign (also for +-inf);
  *   otherwise        -> |f| rounded to the nearest point of the format's grid, ties to the
  *                       point with an even significand; a zero result keeps the sign.
@@ -80,7 +82,7 @@ uint8_t orc_fp8_encode(float f, int fmt)
     double a, maxv, q, r, v;
     int ex, e, ebits, mant;
 
-    if (isnan(f)) return (uint8_t)(0x7F | sign);
+    if (isnan(f)) return 0x7F;
     a = fabs((double)f);
     maxv = orc_fp8_max(fmt);
     if (a > maxv) return (uint8_t)(fmt_maxcode(fmt) | sign);
@@ -116,7 +118,7 @@ uint8_t orc_fp8_encode_search(float f, int fmt)
     uint8_t sign = signbit(f) ? 0x80 : 0x00;
     double a, best_d = INFINITY;
     int c, best = 0;
-    if (isnan(f)) return (uint8_t)(0x7F | sign);
+    if (isnan(f)) return 0x7F;
     a = fabs((double)f);
     if (a > orc_fp8_max(fmt)) return (uint8_t)(fmt_maxcode(fmt) | sign);   /* saturation, incl. inf */
     for (c = 0; c < 0x80; ++c) {
@@ -218,8 +220,8 @@ float orc_scale_inv(float scale) { return 1.0f / scale; }
 
 /*
  * Delayed-scaling update of T tensors' scales from their amax histories ([WS] Motivations,
- * first bullet: the scale-update kernel and the guard of "amax is too tiny that leads to an
- * infinite scale"; [CG] feature list: amaxes reduced within the current iteration).
+ * first bullet: the scale-update kernel, and a fix for amaxes small enough to make the scale
+ * infinite; [CG] feature list: amaxes reduced within the current iteration).
  *
  * hist is [L][T] float32, row 0 = the current iteration's amaxes.  For each tensor t:
  *   a      = max over the L rows of hist[.][t]          (the current amax and L-1 earlier ones)

@@ -1,0 +1,50 @@
+"""Shared helpers of the GPU parity tests: host <-> device copies of bit patterns and the
+GEMM tolerance.  No arithmetic of the method lives here."""
+import numpy as np
+import torch
+
+DEV = "cuda:0"
+
+
+def bf16_dev(a: np.ndarray) -> torch.Tensor:
+    """bfloat16 bit patterns (uint16) -> a bfloat16 tensor on the GPU."""
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def bf16_host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def u8_host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().numpy()
+
+
+def f32_bits(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float32).reshape(-1).view(np.uint32)
+
+
+def scalar(v: float) -> torch.Tensor:
+    return torch.tensor([v], dtype=torch.float32, device=DEV)
+
+
+def to_f64(D: torch.Tensor) -> np.ndarray:
+    return D.detach().float().cpu().numpy().astype(np.float64)
+
+
+GEMM_TOL = 2e-3          # normwise, float32 accumulation against the float64 oracle
+BF16_HALF_ULP_REL = 2.0 ** -8   # bfloat16 rounding: |round(v) - v| <= 2^-8 |v|
+
+
+def gemm_close(got: np.ndarray, ref: np.ndarray, bf16_out: bool, scale_ref: float = None):
+    """Normwise check max|D - R| <= 2e-3 * max|R| (fp32 output); a bfloat16 output may also
+    differ by its own rounding, at most 2^-8 |R| per element (plus the float32 part)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    big = scale_ref if scale_ref is not None else float(np.abs(ref).max()) if ref.size else 0.0
+    err = np.abs(got - ref)
+    bound = GEMM_TOL * big + (BF16_HALF_ULP_REL * (np.abs(ref) + GEMM_TOL * big) if bf16_out else 0.0)
+    ok = err <= bound
+    if not np.all(ok):
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"GEMM mismatch at {i}: got {got[i]} ref {ref[i]} err {err[i]} bound "
+                             f"{np.broadcast_to(bound, err.shape)[i]} (max|R| {big})")
+    return float(err.max() / big) if big else 0.0

@@ -1,0 +1,180 @@
+"""GPU parity of the FP8 GEMM with dequantisation and bias against the float64 oracle, the
+N-chunked variant (bit-identical to the unchunked call, also as a replayed graph) and
+determinism."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_delayed_scaling_amd as F
+import oracle
+import synthetic as S
+from helpers import DEV, bf16_dev, gemm_close, scalar, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _codes(seed, shape, fmt, std=1.0, scale=1.0):
+    """Seeded FP8 operands: cast of seeded bfloat16 by the oracle (host)."""
+    return oracle.cast_amax(S.normal_bf16(seed, shape, std), scale, fmt)[0]
+
+
+def _u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _run(A8, fa, sa, B8, fb, sb, bias_h, out_dtype):
+    M, N = A8.shape[0], B8.shape[0]
+    D = torch.full((M, N), float("nan"), device=DEV, dtype=torch.bfloat16 if out_dtype == 0 else torch.float32)
+    F.fp8_gemm_bias(_u8(A8), fa, scalar(sa), _u8(B8), fb, scalar(sb), None if bias_h is None else bf16_dev(bias_h), D)
+    torch.cuda.synchronize()
+    return D
+
+
+SHAPES = [(1, 1, 16), (37, 45, 48), (256, 256, 128), (300, 520, 272), (513, 257, 1040), (128, 256, 256)]
+
+
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_gemm_parity_small(fa, fb, shape):
+    M, N, K = shape
+    print(f"gemm fa={fa} fb={fb} M={M} N={N} K={K}", flush=True)
+    A8 = _codes(S.seed_for(20, fa), (M, K), fa, 2.0)
+    B8 = _codes(S.seed_for(21, fb), (N, K), fb, 2.0)
+    bias = S.normal_bf16(S.seed_for(22, 0), (N,), 0.1)
+    R = oracle.gemm_bias(A8, fa, 0.5, B8, fb, 0.25, bias)
+    for out_dtype in (0, 1):
+        D = _run(A8, fa, 0.5, B8, fb, 0.25, bias, out_dtype)
+        gemm_close(to_f64(D), R, bf16_out=(out_dtype == 0))
+    D = _run(A8, fa, 0.5, B8, fb, 0.25, None, 1)
+    gemm_close(to_f64(D), oracle.gemm_bias(A8, fa, 0.5, B8, fb, 0.25, None), bf16_out=False)
+
+
+def test_gemm_exact_integer_products():
+    """Small-integer codes: every partial sum is an integer below 2^24, so the float32
+    accumulation is exact and the result must equal the oracle exactly."""
+    M, N, K = 300, 280, 512
+    rng = np.random.default_rng(5)
+    tab = np.array([0x00, 0x38, 0x40, 0x44, 0x48], np.uint8)   # 0 1 2 3 4 in E4M3
+    A8 = tab[rng.integers(0, 5, (M, K))] | np.where(rng.random((M, K)) < 0.5, 0x80, 0).astype(np.uint8)
+    B8 = tab[rng.integers(0, 5, (N, K))]
+    D = _run(A8, 0, 1.0, B8, 0, 1.0, None, 1)
+    assert np.array_equal(to_f64(D), oracle.gemm_bias(A8, 0, 1.0, B8, 0, 1.0))
+
+
+def test_gemm_k_zero_gives_bias_and_empty_mn():
+    bias = S.normal_bf16(3, (40,), 1.0)
+    D = torch.empty((7, 40), device=DEV, dtype=torch.float32)
+    F.fp8_gemm_bias(torch.empty((7, 0), dtype=torch.uint8, device=DEV), 0, scalar(1.0),
+                    torch.empty((40, 0), dtype=torch.uint8, device=DEV), 0, scalar(1.0), bf16_dev(bias), D)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_f64(D), np.tile(S.bf16_bits_to_f64(bias), (7, 1)))
+    D0 = torch.full((0, 5), 1.0, device=DEV)
+    F.fp8_gemm_bias(torch.empty((0, 16), dtype=torch.uint8, device=DEV), 0, scalar(1.0),
+                    torch.empty((5, 16), dtype=torch.uint8, device=DEV), 0, scalar(1.0), None, D0)
+
+
+def test_gemm_strided_operands():
+    """Leading dimensions larger than K (views into wider buffers)."""
+    M, N, K = 200, 150, 96
+    Aw = _codes(30, (M, 160), 0)
+    Bw = _codes(31, (N, 128), 1)
+    A8, B8 = Aw[:, :K], Bw[:, :K]
+    Dw = torch.zeros((M, 168), device=DEV, dtype=torch.float32)
+    D = Dw[:, :N]
+    F.fp8_gemm_bias(_u8(Aw)[:, :K], 0, scalar(1.0), _u8(Bw)[:, :K], 1, scalar(1.0), None, D)
+    torch.cuda.synchronize()
+    gemm_close(to_f64(D), oracle.gemm_bias(A8, 0, 1.0, B8, 1, 1.0), bf16_out=False)
+    assert torch.all(Dw[:, N:] == 0)
+
+
+def test_gemm_deterministic():
+    A8 = _codes(40, (1024, 2048), 0)
+    B8 = _codes(41, (768, 2048), 0)
+    D1 = _run(A8, 0, 1.0, B8, 0, 1.0, None, 1)
+    D2 = _run(A8, 0, 1.0, B8, 0, 1.0, None, 1)
+    assert torch.equal(D1.view(torch.int32), D2.view(torch.int32))
+
+
+def _full_config(M, N, K, fa, fb, seed_base, stdA, stdB, scaleA, scaleB):
+    A8 = _codes(seed_base, (M, K), fa, stdA, scaleA)
+    B8 = _codes(seed_base + 1, (N, K), fb, stdB, scaleB)
+    return A8, B8
+
+
+@pytest.mark.parametrize("which", ["fwd", "dgrad", "wgrad"])
+def test_gemm_full_size_qkv_sampled(which):
+    """The GPT-175B QKV projection at one TP=2 rank's share (M=8192, K=12288, N=18432) in the
+    launch configuration the benchmark times, checked on 16 seeded full rows and 16 seeded full
+    columns of the output against the float64 oracle."""
+    M, K, N = 8192, 12288, 18432
+    if which == "fwd":
+        shapes = (M, N, K, 0, 0)          # x8 [M,K] . W8 [N,K]
+    elif which == "dgrad":
+        shapes = (M, K, N, 1, 0)          # dy8 [M,N] . W8t [K,N]
+    else:
+        shapes = (N, K, M, 1, 0)          # dy8t [N,M] . x8t [K,M]
+    m, n, k, fa, fb = shapes
+    print(f"full-size {which}: M={m} N={n} K={k}", flush=True)
+    A8 = _codes(S.seed_for(4, 10), (m, k), fa, 1.0, 1.0 if fa == 0 else 1.0)
+    B8 = _codes(S.seed_for(4, 11), (n, k), fb, 0.02, 64.0)
+    bias = S.normal_bf16(S.seed_for(4, 12), (n,), 0.1) if which == "fwd" else None
+    D = torch.empty((m, n), device=DEV, dtype=torch.bfloat16)
+    F.fp8_gemm_bias(_u8(A8), fa, scalar(1.0), _u8(B8), fb, scalar(1.0 / 64.0), None if bias is None else bf16_dev(bias), D)
+    torch.cuda.synchronize()
+    rows = (S.uniform(S.seed_for(4, 13), 0, 16) * m).astype(np.int64)
+    cols = (S.uniform(S.seed_for(4, 14), 0, 16) * n).astype(np.int64)
+    Rr, Rc = oracle.gemm_bias_sampled(A8, fa, 1.0, B8, fb, 1.0 / 64.0, bias, rows, cols)
+    Dh = to_f64(D)
+    big = max(float(np.abs(Rr).max()), float(np.abs(Rc).max()))
+    gemm_close(Dh[rows], Rr, bf16_out=True, scale_ref=big)
+    gemm_close(Dh[:, cols], Rc, bf16_out=True, scale_ref=big)
+
+
+@pytest.mark.parametrize("n_chunks", [4, 8])
+def test_chunked_equals_unchunked_and_graph(n_chunks):
+    """N-chunked GEMM+bias (M=8192, K=N=12288), one stream per chunk with its own bias offset,
+    is bit-identical to the unchunked call, eagerly and as a captured, replayed graph."""
+    M, K, N = 8192, 12288, 12288
+    print(f"chunked n_chunks={n_chunks}", flush=True)
+    A8 = _u8(_codes(S.seed_for(5, 0), (M, K), 0, 1.0))
+    B8 = _u8(_codes(S.seed_for(5, 1), (N, K), 0, 0.02, 64.0))
+    bias = bf16_dev(S.normal_bf16(S.seed_for(5, 2), (N,), 0.1))
+    sa, sb = scalar(1.0), scalar(1.0 / 64)
+    ref = torch.empty((M, N), device=DEV, dtype=torch.bfloat16)
+    F.fp8_gemm_bias(A8, 0, sa, B8, 0, sb, bias, ref)
+    streams = [torch.cuda.Stream() for _ in range(n_chunks)]
+    D = torch.zeros((M, N), device=DEV, dtype=torch.bfloat16)
+    F.fp8_gemm_bias_chunked(A8, 0, sa, B8, 0, sb, bias, D, n_chunks, streams)
+    torch.cuda.synchronize()
+    assert torch.equal(D.view(torch.int16), ref.view(torch.int16))
+    # graph capture of the whole fork/join sequence, replayed several times
+    G = torch.zeros((M, N), device=DEV, dtype=torch.bfloat16)
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cap):
+        F.fp8_gemm_bias_chunked(A8, 0, sa, B8, 0, sb, bias, G, n_chunks, streams, stream=cap)
+    for _ in range(3):
+        G.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(G.view(torch.int16), ref.view(torch.int16))
+    # sampled oracle check of the chunked output
+    rows = (S.uniform(S.seed_for(5, 3), 0, 8) * M).astype(np.int64)
+    Rr, _ = oracle.gemm_bias_sampled(A8.cpu().numpy(), 0, 1.0, B8.cpu().numpy(), 0, 1.0 / 64,
+                                     S.normal_bf16(S.seed_for(5, 2), (N,), 0.1), rows, [0])
+    gemm_close(to_f64(G)[rows], Rr, bf16_out=True)
+
+
+def test_chunked_single_stream_and_ragged_chunks():
+    M, K, N = 300, 256, 1000
+    A8 = _codes(60, (M, K), 1)
+    B8 = _codes(61, (N, K), 0)
+    bias = S.normal_bf16(62, (N,), 0.5)
+    ref = _run(A8, 1, 1.0, B8, 0, 1.0, bias, 1)
+    for n_chunks in (1, 3, 7, 16):
+        D = torch.zeros((M, N), device=DEV, dtype=torch.float32)
+        F.fp8_gemm_bias_chunked(_u8(A8), 1, scalar(1.0), _u8(B8), 0, scalar(1.0), bf16_dev(bias), D, n_chunks, None)
+        torch.cuda.synchronize()
+        assert torch.equal(D.view(torch.int32), ref.view(torch.int32)), n_chunks
