@@ -1,0 +1,384 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 delayed-scaling linear-layer path on one MI355X.
+
+One step = one training iteration of an FP8 linear layer at the GPT-175B QKV projection shape
+of one TP=2 rank (tokens M = 8192 = seq 2048 x batch 4, K = 12288, N = 18432), every kernel
+of the path in the order a training iteration runs them:
+  forward : cast+transpose x (E4M3), cast+transpose W (E4M3), FP8 GEMM + bias -> y (bf16)
+  backward: dbias + cast+transpose dy (E5M2), dgrad GEMM -> dx (bf16), wgrad GEMM -> dW (fp32)
+  recipe  : fused amax-history scale update of the three tensors (history length 1024)
+Inputs are seeded synthetic bf16 tensors already resident in HBM; the step time includes
+every launch.  `value` is the three GEMMs' 2*M*N*K FLOPs per step over the step time.
+
+Also reported (own timings, HIP events on the launch stream):
+  * per-kernel average durations inside the timed steps, the GEMM roofline fraction;
+  * cast+transpose sweep at [8192, 12288] with cold caches (GB/s, % of 8 TB/s);
+  * dbias+cast+transpose of dy [8192, 4096] and the T=3, L=1024 scale update;
+  * the forward-only small layer ([128,256] x [256,256]): eager and graph-replay latency;
+  * N-chunked GEMM+bias M=8192, K=N=12288 in 4 and 8 chunks on their own streams, as a graph;
+  * the CPU oracle on a bounded sample of the same step (baseline only).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+FP8_PEAK = 5.0e15          # FLOP/s, MI355X dense FP8 MFMA
+
+M, K, N = 8192, 12288, 18432
+HIST_L = 1024
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-extras", action="store_true", help="only the timed training step")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
+                                   "not implemented (run with --gpus 1)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp8_delayed_scaling_amd as F
+    import synthetic as S
+
+    F.lib()   # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t0 = time.time()
+    x_h = S.normal_bf16(S.seed_for(4, 0), (M, K), 1.0)
+    w_h = S.normal_bf16(S.seed_for(4, 1), (N, K), 0.02)
+    b_h = S.normal_bf16(S.seed_for(4, 2), (N,), 0.1)
+    dy_h = S.normal_bf16(S.seed_for(4, 3), (M, N), 0.01)
+    x, w, b, dy = bf16(x_h), bf16(w_h), bf16(b_h), bf16(dy_h)
+    log(f"inputs generated and uploaded in {time.time() - t0:.1f}s")
+
+    u8 = dict(device=dev, dtype=torch.uint8)
+    f32 = dict(device=dev, dtype=torch.float32)
+    hist = torch.zeros((HIST_L, 3), **f32)
+    scale = torch.ones(3, **f32)
+    scale_inv = torch.ones(3, **f32)
+    sinv = torch.zeros(3, **f32)
+    x8, x8t = torch.empty((M, K), **u8), torch.empty((K, M), **u8)
+    w8, w8t = torch.empty((N, K), **u8), torch.empty((K, N), **u8)
+    dy8, dy8t = torch.empty((M, N), **u8), torch.empty((N, M), **u8)
+    y = torch.empty((M, N), device=dev, dtype=torch.bfloat16)
+    dx = torch.empty((M, K), device=dev, dtype=torch.bfloat16)
+    dw = torch.empty((N, K), **f32)
+    db = torch.empty(N, **f32)
+    ws = torch.empty(F.fp8_dbias_workspace_bytes(M, N), **u8)
+    fmts = [F.E4M3, F.E4M3, F.E5M2]
+
+    names = ["cast_transpose_x", "cast_transpose_w", "gemm_fwd", "dbias_cast_transpose_dy", "gemm_dgrad",
+             "gemm_wgrad", "scale_update"]
+
+    def step(ev=None):
+        """One training iteration; `ev` (list of event pairs) brackets each launch when given."""
+        calls = [
+            lambda: F.fp8_cast_transpose(x, scale[0:1], F.E4M3, x8, x8t, sinv[0:1], hist[0, 0:1]),
+            lambda: F.fp8_cast_transpose(w, scale[1:2], F.E4M3, w8, w8t, sinv[1:2], hist[0, 1:2]),
+            lambda: F.fp8_gemm_bias(x8, F.E4M3, sinv[0:1], w8, F.E4M3, sinv[1:2], b, y),
+            lambda: F.fp8_dbias_cast_transpose(dy, scale[2:3], F.E5M2, dy8, dy8t, db, ws, sinv[2:3], hist[0, 2:3]),
+            lambda: F.fp8_gemm_bias(dy8, F.E5M2, sinv[2:3], w8t, F.E4M3, sinv[1:2], None, dx),
+            lambda: F.fp8_gemm_bias(dy8t, F.E5M2, sinv[2:3], x8t, F.E4M3, sinv[0:1], None, dw),
+            lambda: F.fp8_scale_update(hist, scale, scale_inv, fmts, 0),
+        ]
+        for i, c in enumerate(calls):
+            if ev is not None:
+                ev[i][0].record()
+            c()
+            if ev is not None:
+                ev[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, events around every launch
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
+           for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        step(evs[s])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    per_kernel = {n: float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]))
+                  for i, n in enumerate(names)}
+    gemm_flop = 2.0 * M * N * K
+    step_flop = 3 * gemm_flop
+    value = step_flop / (ms_step * 1e-3) / 1e12
+    gemm_ms = float(np.mean([per_kernel["gemm_fwd"], per_kernel["gemm_dgrad"], per_kernel["gemm_wgrad"]]))
+    gemm_tflops = gemm_flop / (gemm_ms * 1e-3) / 1e12
+    log(f"step {ms_step:.3f} ms ({value:.1f} TFLOP/s), per kernel ms: "
+        + ", ".join(f"{k}={v:.4f}" for k, v in per_kernel.items()))
+
+    # bytes of the cast kernels (algorithmic: read bf16, write two FP8 copies)
+    ct_x_bytes = M * K * 4
+    ct_w_bytes = N * K * 4
+    dct_bytes = M * N * 4 + N * 4
+
+    traffic = _traffic_record()
+
+    result = {
+        "metric": "FP8 linear fwd+bwd TFLOP/s + cast_transpose GB/s, % of MI355X peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic (seeded normal bf16: x~N(0,1), W~N(0,0.02), bias~N(0,0.1), dy~N(0,0.01))",
+        "config": {
+            "workload": "FP8 linear training step, GPT-175B QKV projection at one TP=2 rank's share: "
+                        "M=8192 tokens (seq 2048 x batch 4), K=12288, N=18432; fwd + bwd + scale update",
+            "M": M, "K": K, "N": N, "amax_history": HIST_L, "formats": "x,W E4M3; dy E5M2",
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "k_gemm_bias (fwd/dgrad/wgrad average)",
+            "achieved": round(gemm_tflops, 2),
+            "peak": FP8_PEAK / 1e12,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops * 1e12 / FP8_PEAK, 4),
+            "traffic": traffic,
+        },
+        "kernels_ms": {k: round(v, 4) for k, v in per_kernel.items()},
+        "step_breakdown": {
+            "gemm_tflops_each": {k: round(gemm_flop / (per_kernel[k] * 1e-3) / 1e12, 1)
+                                 for k in ("gemm_fwd", "gemm_dgrad", "gemm_wgrad")},
+            "cast_transpose_x_GBps": round(ct_x_bytes / (per_kernel["cast_transpose_x"] * 1e-3) / 1e9, 1),
+            "cast_transpose_w_GBps": round(ct_w_bytes / (per_kernel["cast_transpose_w"] * 1e-3) / 1e9, 1),
+            "dbias_cast_transpose_dy_GBps": round(dct_bytes / (per_kernel["dbias_cast_transpose_dy"] * 1e-3) / 1e9, 1),
+            "gemm_only_tflops": round(step_flop / (3 * gemm_ms * 1e-3) / 1e12, 1),
+            "host_wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        },
+    }
+    del evs
+
+    if not args.no_extras:
+        result["extras"] = extras(F, S, torch, np, dev, bf16)
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(x_h, w_h, b_h, dy_h)
+
+    print(json.dumps(result))
+
+
+def _traffic_record():
+    """HBM traffic of the GEMM from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel source (its sha256 is stored with the counters); otherwise null."""
+    path = os.path.join(ROOT, "profiles", "gemm_fp8_qkv_counters.json")
+    src = os.path.join(ROOT, "fp8_delayed_scaling_amd", "csrc", "gemm.hip")
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec.get("gemm_source_sha256") != h:
+            return None
+        return rec.get("traffic_bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def _time_fn(torch, fn, reps=20):
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def extras(F, S, torch, np, dev, bf16):
+    out = {}
+    u8 = dict(device=dev, dtype=torch.uint8)
+    f32 = dict(device=dev, dtype=torch.float32)
+    flush = torch.empty(512 << 20, **u8)     # 512 MB: evicts the 256 MB MALL and the L2s
+
+    def cold_time(fn, reps=10):
+        ts = []
+        for _ in range(reps):
+            flush.zero_()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            ts.append(s.elapsed_time(e))
+        return float(np.median(ts))
+
+    # cast+transpose sweep (steady-state scale of its outlier tensors), cold caches
+    sweep = {}
+    for idx, (R, C) in enumerate([(1024, 1024), (4096, 4096), (8192, 12288)]):
+        xh = S.outlier_bf16(S.seed_for(1, idx), (R, C), 1.0)
+        xd = bf16(xh)
+        o, ot = torch.empty((R, C), **u8), torch.empty((C, R), **u8)
+        sc, si, am = torch.tensor([0.4], **f32), torch.zeros(1, **f32), torch.zeros(1, **f32)
+        F.fp8_cast_transpose(xd, sc, F.E4M3, o, ot, si, am)
+        ms = cold_time(lambda: F.fp8_cast_transpose(xd, sc, F.E4M3, o, ot, si, am))
+        gbps = R * C * 4 / (ms * 1e-3) / 1e9
+        sweep[f"{R}x{C}"] = {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1), "frac_hbm": round(gbps * 1e9 / HBM_PEAK, 3)}
+        del xd, o, ot
+    out["cast_transpose_sweep_cold"] = sweep
+
+    # cast+amax (row-major only) at the same large shape, cold
+    xh = S.outlier_bf16(S.seed_for(1, 2), (8192, 12288), 1.0)
+    xd = bf16(xh)
+    o = torch.empty((8192 * 12288,), **u8)
+    sc, si, am = torch.tensor([0.4], **f32), torch.zeros(1, **f32), torch.zeros(1, **f32)
+    ms = cold_time(lambda: F.fp8_cast_amax(xd, sc, F.E4M3, o, si, am))
+    out["cast_amax_8192x12288_cold"] = {"us": round(ms * 1e3, 2), "GBps": round(8192 * 12288 * 3 / (ms * 1e-3) / 1e9, 1)}
+    del xd, o
+
+    # backward prep: dbias + cast+transpose dy [8192, 4096] E5M2; scale update L=1024, T=3
+    R, C = 8192, 4096
+    dyd = bf16(S.normal_bf16(S.seed_for(3, 0), (R, C), 0.01))
+    o, ot = torch.empty((R, C), **u8), torch.empty((C, R), **u8)
+    dbb = torch.empty(C, **f32)
+    wsb = torch.empty(F.fp8_dbias_workspace_bytes(R, C), **u8)
+    sc, si, am = torch.tensor([4096.0], **f32), torch.zeros(1, **f32), torch.zeros(1, **f32)
+    ms = cold_time(lambda: F.fp8_dbias_cast_transpose(dyd, sc, F.E5M2, o, ot, dbb, wsb, si, am))
+    h = torch.from_numpy(S.log_uniform_f32(S.seed_for(3, 1), 1024 * 3, 1e-3, 1e3).reshape(1024, 3)).to(dev)
+    s3, si3 = torch.ones(3, **f32), torch.ones(3, **f32)
+    F.fp8_scale_update(h, s3, si3, [0, 0, 1], 0)
+    torch.cuda.synchronize()
+    us_upd = _time_fn(torch, lambda: F.fp8_scale_update(h, s3, si3, [0, 0, 1], 0), 50) * 1e3
+    out["backward_prep"] = {"dbias_cast_transpose_8192x4096_us": round(ms * 1e3, 2),
+                            "GBps": round((R * C * 4 + C * 4) / (ms * 1e-3) / 1e9, 1),
+                            "scale_update_L1024_T3_us": round(us_upd, 2)}
+    del dyd, o, ot
+
+    # small forward layer: eager call vs graph replay
+    Ms, Ns, Ks = 128, 256, 256
+    xs, wsm, bs = bf16(S.normal_bf16(S.seed_for(0, 0), (Ms, Ks), 1.0)), bf16(S.normal_bf16(S.seed_for(0, 1), (Ns, Ks), 1.0)), \
+        bf16(S.normal_bf16(S.seed_for(0, 2), (Ns,), 0.1))
+    hs, ss, sis = torch.zeros((16, 3), **f32), torch.ones(3, **f32), torch.zeros(3, **f32)
+    x8s, w8s, w8ts = torch.empty((Ms, Ks), **u8), torch.empty((Ns, Ks), **u8), torch.empty((Ks, Ns), **u8)
+    ys = torch.empty((Ms, Ns), device=dev, dtype=torch.bfloat16)
+
+    def small_fwd(stream=None):
+        F.fp8_linear_fwd(xs, wsm, bs, ss[0:1], hs[0, 0:1], x8s, None, sis[0:1], ss[1:2], hs[0, 1:2], w8s, w8ts,
+                         sis[1:2], None, ys, stream=stream)
+
+    small_fwd()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(200):
+        small_fwd()
+    torch.cuda.synchronize()
+    eager_us = (time.perf_counter() - t) / 200 * 1e6
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        small_fwd(stream=cap)
+    g.replay()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(200):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_us = (time.perf_counter() - t) / 200 * 1e6
+    out["small_forward_128x256x256"] = {"eager_us_per_call": round(eager_us, 2), "graph_replay_us": round(graph_us, 2),
+                                        "launches": 3}
+
+    # N-chunked GEMM + bias, M=8192, K=N=12288, one stream per chunk, captured as one graph
+    Mc, Kc, Nc = 8192, 12288, 12288
+    def codes(seed, rows):
+        """Seeded finite E4M3 codes (exponent field even, so never the NaN code), mixed signs."""
+        c = torch.randint(0, 256, (rows, Kc), generator=torch.Generator().manual_seed(seed), dtype=torch.uint8)
+        return (c & 0xF7).to(dev)
+
+    A8 = codes(7, Mc)
+    B8 = codes(8, Nc)
+    biasc = bf16(S.normal_bf16(S.seed_for(5, 2), (Nc,), 0.1))
+    sa, sb = torch.tensor([1.0], **f32), torch.tensor([1.0], **f32)
+    D = torch.empty((Mc, Nc), device=dev, dtype=torch.bfloat16)
+    flop = 2.0 * Mc * Nc * Kc
+    F.fp8_gemm_bias(A8, 0, sa, B8, 0, sb, biasc, D)
+    torch.cuda.synchronize()
+    res = {"unchunked_tflops": round(flop / (_time_fn(torch, lambda: F.fp8_gemm_bias(A8, 0, sa, B8, 0, sb, biasc, D), 10)
+                                            * 1e-3) / 1e12, 1)}
+    for nch in (4, 8):
+        streams = [torch.cuda.Stream() for _ in range(nch)]
+        cap = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        F.fp8_gemm_bias_chunked(A8, 0, sa, B8, 0, sb, biasc, D, nch, streams)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            F.fp8_gemm_bias_chunked(A8, 0, sa, B8, 0, sb, biasc, D, nch, streams, stream=cap)
+        g.replay()
+        torch.cuda.synchronize()
+        ms = _time_fn(torch, g.replay, 10)
+        res[f"chunks{nch}_graph_tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
+    out["chunked_gemm_8192x12288x12288"] = res
+    del A8, B8, D, flush
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(x_h, w_h, b_h, dy_h):
+    """The oracle (as it stands) on a bounded sample of the step: 16 of the 8192 token rows of
+    x and dy with the full weight.  Single thread (the C oracle is scalar; BLAS limited to 1)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    rows = 16
+    xs = np.ascontiguousarray(x_h[:rows])
+    dys = np.ascontiguousarray(dy_h[:rows])
+    with threadpool_limits(limits=1):
+        t = time.perf_counter()
+        f = oracle.linear_fwd(xs, w_h, b_h, 1.0, 1.0)
+        bw = oracle.linear_bwd(dys, 1.0, f["x8t"], f["x_sinv"], f["w8t"], f["w_sinv"])
+        h = np.zeros((HIST_L, 3), np.float32)
+        h[0] = [f["x_amax"], f["w_amax"], bw["dy_amax"]]
+        oracle.scale_update(h, np.ones(3, np.float32), np.ones(3, np.float32), [0, 0, 1], 0)
+        sec = time.perf_counter() - t
+    flop = 3 * 2.0 * rows * N * K
+    return {"value": round(flop / sec / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "seconds": round(sec, 2),
+            "sample": f"one training step on {rows} of the {M} token rows of x and dy with the full "
+                      f"[{N},{K}] weight (W cast+transpose, three float64 GEMMs, dbias, scale update); "
+                      f"FLOPs counted as 3 x 2 x {rows} x {N} x {K}"}
+
+
+if __name__ == "__main__":
+    main()
