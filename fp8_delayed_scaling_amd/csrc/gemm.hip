@@ -7,23 +7,29 @@
 // fix).  Both operands are K-contiguous ("TN"); the transposes the backward needs come from
 // the cast+transpose kernels, so the GEMM never transposes.
 //
-// Design (CDNA4):
-//   * block tile 256 x 256, K step 128 bytes, 256 threads = 4 waves in a 2 x 2 grid, each wave
-//     a 128 x 128 sub-tile made of 4 x 4 v_mfma_f32_32x32x64_f8f6f4 tiles (float32 accumulate;
-//     the A / B formats are the instruction's cbsz / blgp selectors, so E4M3 x E4M3,
-//     E5M2 x E4M3 and the others share one kernel template);
-//   * global -> registers -> LDS, double-buffered LDS (2 x 64 KB of the 160 KB), one barrier per
-//     K step, the next K step's global loads in flight during the current step's MFMAs;
-//   * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
-//     c ^ (r & 7) ^ ((r >> 3) & 1), so the 32 rows one MFMA operand read touches spread over
-//     all banks;
-//   * blocks are remapped so that each XCD (blocks are dealt round-robin to the 8 XCDs) works
-//     on a contiguous range of tiles, walked in groups of 8 tile-rows for L2 reuse;
-//   * epilogue: acc * a_scale_inv * b_scale_inv + bias in float32, rounded to bfloat16 (nearest
-//     even) or stored as float32.
-// Ragged M / N are handled by clamping the rows that are loaded and masking the stores; a
-// ragged K (a multiple of 16) by zero-filling the 16-byte chunks past K.  No split-K: every
-// output element is one fixed sequence of MFMAs over K, whatever tile it falls in.
+// Both kernels: block tile 256 x 256, 256 threads = 4 waves in a 2 x 2 grid, each wave a 128 x 128
+// sub-tile made of 4 x 4 v_mfma_f32_32x32x64_f8f6f4 tiles (float32 accumulate; the A / B formats
+// are the instruction's cbsz / blgp selectors, so every format pair shares one template).
+// Blocks are remapped so that each XCD (blocks are dealt round-robin to the 8 XCDs) works on a
+// contiguous range of tiles, walked in groups of kGroupM tile-rows for L2 reuse.  Epilogue:
+// acc * a_scale_inv * b_scale_inv + bias in float32, rounded to bfloat16 (nearest even) or stored
+// as float32.  Ragged M / N are handled by clamping the rows that are loaded and masking the
+// stores.  No split-K: every output element is one fixed sequence of MFMAs over K in the same
+// K order in both kernels, whatever tile it falls in.
+//
+// k_gemm_bias_pipe (K % 64 == 0, the hot path): a 4-stage pipeline of 64-byte K slices
+// (4 x 32 KB of LDS).  Global memory goes straight into LDS with global_load_lds_dwordx4 (no
+// staging registers), three slices ahead of the MFMAs; each wave prefetches the next slice's
+// operand fragments from LDS while its MFMAs run on the current ones (double-buffered
+// fragments), and the instruction scheduler is told to interleave one MFMA with one LDS read and
+// every other MFMA with one global load.  The four stages are four distinct LDS arrays so the
+// compiler can tell the in-flight loads of one stage from the reads of another, and the
+// per-slice barrier is a bare s_barrier after an explicit vmcnt wait (a fenced barrier would
+// drain every load in flight).  LDS rows are 64 bytes; 16-byte chunk c of row r sits at chunk
+// c ^ ((r >> 2) & 3), which measured bank-conflict free for the MFMA operand reads.
+//
+// k_gemm_bias (any K % 16 == 0): global -> registers -> LDS with double-buffered 128-byte K
+// slices, the K tail zero-filled.
 #include "device_common.h"
 #include "launch.h"
 
@@ -35,12 +41,27 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 namespace {
 constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int kThreads = 256;
-constexpr int kGroupM = 8;
+constexpr int kGroupM = 4;
 constexpr int kLdsA = BM * BK;             // bytes per A buffer
 constexpr int kLdsB = BN * BK;
 constexpr int kLdsBytes = 2 * (kLdsA + kLdsB);
 
 __device__ __forceinline__ int lds_chunk(int row, int c) { return c ^ (row & 7) ^ ((row >> 3) & 1); }
+
+// Tile of this block: XCD-contiguous ranges, walked in groups of kGroupM tile-rows.
+__device__ __forceinline__ void block_tile(int tiles_m, int tiles_n, int &tm, int &tn) {
+    const int nwg = tiles_m * tiles_n;
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, local = bid >> 3;
+    const int q8 = nwg >> 3, r8 = nwg & 7;
+    const int tile = (xcd < r8) ? xcd * (q8 + 1) + local : r8 * (q8 + 1) + (xcd - r8) * q8 + local;
+    const int group = tile / (kGroupM * tiles_n);
+    const int first_m = group * kGroupM;
+    const int gm = min(tiles_m - first_m, kGroupM);
+    const int in_group = tile - group * kGroupM * tiles_n;
+    tm = first_m + in_group % gm;
+    tn = in_group / gm;
+}
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
     uint32_t u = __float_as_uint(v);
@@ -49,6 +70,37 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
     return (uint16_t)(u >> 16);
 }
 }  // namespace
+
+// Epilogue of one wave's 128 x 128 sub-tile at (row0, col0).  Accumulator element e of lane l in
+// a 32 x 32 MFMA tile is row (e / 4) * 8 + (l / 32) * 4 + e % 4, column l % 32.
+template <int OUT>
+__device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], const float *__restrict__ a_sinv,
+                                         const float *__restrict__ b_sinv, const uint16_t *__restrict__ bias,
+                                         void *__restrict__ D, int64_t ldd, int M, int N, int row0, int col0,
+                                         int lane) {
+    const int frow = lane & 31, fhalf = lane >> 5;
+    const float sa = *a_sinv, sb = *b_sinv;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int col = col0 + j * 32 + frow;
+        if (col >= N) continue;
+        const float bv = bias != nullptr ? __uint_as_float((uint32_t)bias[col] << 16) : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = row0 + i * 32 + (e >> 2) * 8 + fhalf * 4 + (e & 3);
+                if (row < M) {
+                    const float v = acc[i][j][e] * sa * sb + bv;
+                    if constexpr (OUT == 0)
+                        reinterpret_cast<uint16_t *>(D)[(int64_t)row * ldd + col] = f32_to_bf16_rne(v);
+                    else
+                        reinterpret_cast<float *>(D)[(int64_t)row * ldd + col] = v;
+                }
+            }
+        }
+    }
+}
 
 template <int FA, int FB, int OUT>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias(const uint8_t *__restrict__ A, int64_t lda,
@@ -60,18 +112,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias(const uint8_t *__rest
                                                            int K, int tiles_m, int tiles_n) {
     __shared__ __align__(16) uint8_t smem[kLdsBytes];
 
-    // ---- tile of this block: XCD-contiguous ranges, grouped row-major walk
-    const int nwg = tiles_m * tiles_n;
-    const int bid = blockIdx.x;
-    const int xcd = bid & 7, local = bid >> 3;
-    const int q8 = nwg >> 3, r8 = nwg & 7;
-    const int tile = (xcd < r8) ? xcd * (q8 + 1) + local : r8 * (q8 + 1) + (xcd - r8) * q8 + local;
-    const int group = tile / (kGroupM * tiles_n);
-    const int first_m = group * kGroupM;
-    const int gm = min(tiles_m - first_m, kGroupM);
-    const int in_group = tile - group * kGroupM * tiles_n;
-    const int tm = first_m + in_group % gm;
-    const int tn = in_group / gm;
+    int tm, tn;
+    block_tile(tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -173,29 +215,165 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias(const uint8_t *__rest
         __syncthreads();
     }
 
-    // ---- epilogue.  Accumulator element e of lane l in a 32 x 32 tile is row
-    //      (e / 4) * 8 + (l / 32) * 4 + e % 4, column l % 32.
-    const float sa = *a_sinv, sb = *b_sinv;
+    epilogue<OUT>(acc, a_sinv, b_sinv, bias, D, ldd, M, N, m0 + wm * 128, n0 + wn * 128, lane);
+}
+
+
+// ------------------------------------------------------------------------------------------
+// k_gemm_bias_pipe: the 4-stage direct-to-LDS pipeline (K % 64 == 0).
+// ------------------------------------------------------------------------------------------
+namespace {
+constexpr int kPK = 64;                          // K bytes per pipeline slice
+constexpr int kPStage = (BM + BN) * kPK;         // 32 KB: A rows then B rows, 64 bytes each
+__device__ __forceinline__ int pswz(int r) { return (r >> 2) & 3; }
+}  // namespace
+
+// vmcnt-only wait: expcnt and lgkmcnt fields left at their maxima (no wait on them).
+#define FP8DS_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0xF70 | ((n) & 0xF) | (((n) >> 4) << 14))
+// Workgroup barrier without a memory fence: the caller has already waited for the loads it
+// needs (a fenced barrier would also wait for the later slices still in flight).  The empty
+// asm statements keep the compiler from moving LDS accesses across it.
+#define FP8DS_BARRIER()                          \
+    do {                                         \
+        asm volatile("" ::: "memory");           \
+        __builtin_amdgcn_s_barrier();            \
+        asm volatile("" ::: "memory");           \
+    } while (0)
+
+template <int FA, int FB, int OUT>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_bias_pipe(const uint8_t *__restrict__ A, int64_t lda,
+                                                                const uint8_t *__restrict__ B, int64_t ldb,
+                                                                const float *__restrict__ a_sinv,
+                                                                const float *__restrict__ b_sinv,
+                                                                const uint16_t *__restrict__ bias,
+                                                                void *__restrict__ D, int64_t ldd, int M, int N,
+                                                                int K, int tiles_m, int tiles_n) {
+    __shared__ __align__(16) uint8_t st0[kPStage];
+    __shared__ __align__(16) uint8_t st1[kPStage];
+    __shared__ __align__(16) uint8_t st2[kPStage];
+    __shared__ __align__(16) uint8_t st3[kPStage];
+
+    int tm, tn;
+    block_tile(tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // Direct loads: a slice is 2048 chunks of 16 bytes; load i of wave w writes the 1 KB of the
+    // stage at (i * 4 + w) * 1024, lane l at + 16 l.  Position p holds row p / 64 (A rows 0-255,
+    // then B rows) and stored chunk (p / 16) % 4, i.e. source chunk stored ^ pswz(row).
+    const uint8_t *src[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 128 + j * 32 + frow;
-        if (col >= N) continue;
-        const float bv = bias != nullptr ? __uint_as_float((uint32_t)bias[col] << 16) : 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = m0 + wm * 128 + i * 32 + (e >> 2) * 8 + fhalf * 4 + (e & 3);
-                if (row < M) {
-                    const float v = acc[i][j][e] * sa * sb + bv;
-                    if constexpr (OUT == 0)
-                        reinterpret_cast<uint16_t *>(D)[(int64_t)row * ldd + col] = f32_to_bf16_rne(v);
-                    else
-                        reinterpret_cast<float *>(D)[(int64_t)row * ldd + col] = v;
-                }
-            }
-        }
+    for (int i = 0; i < 8; ++i) {
+        const int p = (i * 4 + wave) * 1024 + lane * 16;
+        const int row = p >> 6, slot = (p >> 4) & 3;
+        const int r = row & 255;
+        const int c = slot ^ pswz(r);
+        src[i] = row < 256 ? A + (int64_t)min(m0 + r, M - 1) * lda + c * 16
+                           : B + (int64_t)min(n0 + r, N - 1) * ldb + c * 16;
     }
+    const int nk = K / kPK;
+#define FP8DS_ISSUE(ST, kt)                                                                               \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                         \
+        __builtin_amdgcn_global_load_lds((const void *)(src[i] + (int64_t)(kt) * kPK),                    \
+                                         (__attribute__((address_space(3))) void *)((ST) + (i * 4 + wave) * 1024), \
+                                         16, 0, 0);
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    // Operand fragments: lane l supplies row l % 32 of a 32-row MFMA tile and the 32 bytes
+    // [32 (l / 32), +32) of the 64-byte slice, two 16-byte reads.
+    const int frow = lane & 31, fhalf = lane >> 5;
+    int oa0[4], oa1[4], ob0[4], ob1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ra = wm * 128 + i * 32 + frow, rb = wn * 128 + i * 32 + frow;
+        oa0[i] = ra * kPK + (((fhalf * 2) ^ pswz(ra)) << 4);
+        oa1[i] = ra * kPK + (((fhalf * 2 + 1) ^ pswz(ra)) << 4);
+        ob0[i] = BM * kPK + rb * kPK + (((fhalf * 2) ^ pswz(rb)) << 4);
+        ob1[i] = BM * kPK + rb * kPK + (((fhalf * 2 + 1) ^ pswz(rb)) << 4);
+    }
+    auto ld = [&](const uint8_t *st, int o0, int o1) -> i32x8 {
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(st + o0);
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(st + o1);
+        i32x8 r;
+        r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+        r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+        return r;
+    };
+#define FP8DS_FRAGS(ST, FA_, FB_)                                                                          \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                       \
+        FA_[i] = ld((ST), oa0[i], oa1[i]);                                                                \
+        FB_[i] = ld((ST), ob0[i], ob1[i]);                                                                \
+    }
+#define FP8DS_MFMA(CA, CB)                                                                                \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                         \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                         \
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(CA[i], CB[j], acc[i][j], FA, FB, 0, 0, 0, 0);
+    // One slice: wait for slice kt+1, barrier, issue slice kt+3 into the stage slice kt-1 used,
+    // prefetch slice kt+1's fragments, run slice kt's 16 MFMAs (interleaved by the scheduler).
+#define FP8DS_STEP(kt, NXT1, ISS, CA, CB, NA, NB)                                                         \
+    __builtin_amdgcn_sched_barrier(0);                                                                    \
+    FP8DS_WAIT_VM(8);                                                                                     \
+    FP8DS_BARRIER();                                                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                                    \
+    FP8DS_ISSUE(ISS, (kt) + 3)                                                                            \
+    FP8DS_FRAGS(NXT1, NA, NB)                                                                             \
+    FP8DS_MFMA(CA, CB)                                                                                    \
+    _Pragma("unroll") for (int q = 0; q < 16; ++q) {                                                      \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                \
+        if (q & 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                     \
+    }                                                                                                     \
+    __builtin_amdgcn_sched_barrier(0);
+
+    i32x8 fa0[4], fb0[4], fa1[4], fb1[4];
+    // prologue: slices 0..2 in flight, wait for slice 0, fetch its fragments
+    FP8DS_ISSUE(st0, 0)
+    if (nk > 1) { FP8DS_ISSUE(st1, 1) }
+    if (nk > 2) { FP8DS_ISSUE(st2, 2) }
+    if (nk > 2) FP8DS_WAIT_VM(16);
+    else if (nk > 1) FP8DS_WAIT_VM(8);
+    else FP8DS_WAIT_VM(0);
+    FP8DS_BARRIER();
+    FP8DS_FRAGS(st0, fa0, fb0)
+    int kt = 0;
+    // steady state: four slices per trip, every slice issues slice kt+3 (< nk)
+    for (; kt + 6 < nk; kt += 4) {
+        FP8DS_STEP(kt + 0, st1, st3, fa0, fb0, fa1, fb1)
+        FP8DS_STEP(kt + 1, st2, st0, fa1, fb1, fa0, fb0)
+        FP8DS_STEP(kt + 2, st3, st1, fa0, fb0, fa1, fb1)
+        FP8DS_STEP(kt + 3, st0, st2, fa1, fb1, fa0, fb0)
+    }
+    // remaining slices (fewer than 7): everything in flight is waited for, fragments re-read
+    for (; kt < nk; ++kt) {
+        FP8DS_WAIT_VM(0);
+        FP8DS_BARRIER();
+        if (kt + 3 < nk) {
+            const int s3 = (kt + 3) & 3;
+            if (s3 == 0) { FP8DS_ISSUE(st0, kt + 3) }
+            else if (s3 == 1) { FP8DS_ISSUE(st1, kt + 3) }
+            else if (s3 == 2) { FP8DS_ISSUE(st2, kt + 3) }
+            else { FP8DS_ISSUE(st3, kt + 3) }
+        }
+        const int sc = kt & 3;
+        const uint8_t *cur = sc == 0 ? st0 : sc == 1 ? st1 : sc == 2 ? st2 : st3;
+        i32x8 ta[4], tb[4];
+        FP8DS_FRAGS(cur, ta, tb)
+        FP8DS_MFMA(ta, tb)
+    }
+#undef FP8DS_ISSUE
+#undef FP8DS_FRAGS
+#undef FP8DS_MFMA
+#undef FP8DS_STEP
+    epilogue<OUT>(acc, a_sinv, b_sinv, bias, D, ldd, M, N, m0 + wm * 128, n0 + wn * 128, lane);
 }
 
 // D = bias broadcast (K == 0): no products at all.
@@ -225,9 +403,16 @@ hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64
     }
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
     dim3 grid((unsigned)(tiles_m * tiles_n));
+    const bool pipe = (K % kPK) == 0;
 #define FP8DS_GEMM(FA_, FB_, O_)                                                                           \
-    k_gemm_bias<FA_, FB_, O_><<<grid, dim3(kThreads), 0, st>>>(A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, \
-                                                               (int)M, (int)N, (int)K, tiles_m, tiles_n)
+    do {                                                                                                   \
+        if (pipe)                                                                                          \
+            k_gemm_bias_pipe<FA_, FB_, O_><<<grid, dim3(kThreads), 0, st>>>(                               \
+                A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, tiles_m, tiles_n);   \
+        else                                                                                               \
+            k_gemm_bias<FA_, FB_, O_><<<grid, dim3(kThreads), 0, st>>>(                                    \
+                A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, tiles_m, tiles_n);   \
+    } while (0)
     const int sel = fa * 4 + fb * 2 + out_dtype;
     switch (sel) {
         case 0: FP8DS_GEMM(kE4M3, kE4M3, 0); break;
