@@ -44,7 +44,36 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-extras", action="store_true", help="only the timed training step")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--traffic-probe", action="store_true",
+                   help="only launch one plain 1 GiB device copy and one forward GEMM (for rocprofv3 --pmc "
+                        "FETCH_SIZE / WRITE_SIZE passes: the copy calibrates the counters)")
     return p.parse_args()
+
+
+def traffic_probe():
+    """One plain copy of 1 GiB (known traffic: 1 GiB read + 1 GiB written) and one forward GEMM
+    launch at the QKV shape, nothing else on the GPU, so per-dispatch counters of the two can be
+    compared."""
+    import torch
+
+    import fp8_delayed_scaling_amd as F
+
+    F.lib()
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(11)
+    src = torch.randint(0, 256, (1 << 30,), dtype=torch.uint8, generator=g).to(dev)
+    dst = torch.empty_like(src)
+    a8 = (torch.randint(0, 256, (M, K), dtype=torch.uint8, generator=g) & 0xF7).to(dev)
+    b8 = (torch.randint(0, 256, (N, K), dtype=torch.uint8, generator=g) & 0xF7).to(dev)
+    bias = torch.zeros(N, device=dev, dtype=torch.bfloat16)
+    y = torch.empty((M, N), device=dev, dtype=torch.bfloat16)
+    one = torch.ones(1, device=dev)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    F.fp8_gemm_bias(a8, F.E4M3, one, b8, F.E4M3, one, bias, y)
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_probe": "done", "copy_bytes_each_way": 1 << 30, "gemm": [M, N, K]}))
 
 
 def log(*a):
@@ -53,6 +82,9 @@ def log(*a):
 
 def main():
     args = parse()
+    if args.traffic_probe:
+        traffic_probe()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
                                    "not implemented (run with --gpus 1)"}))
