@@ -17,9 +17,9 @@
 namespace fp8ds {
 
 // ------------------------------------------------------------------------------------------
-// 1-D cast + amax.  Each thread converts 32 elements per step (four 16-byte loads in flight,
-// two 16-byte stores) in a grid-stride loop; a remainder of up to 31 elements is converted
-// element by element.
+// 1-D cast + amax.  A thread converts two 16-element groups per step (four 16-byte loads in
+// flight, a grid-stride apart so each wave's accesses stay contiguous), in a grid-stride loop
+// over at most 2048 blocks; a remainder of up to 15 elements is converted element by element.
 // ------------------------------------------------------------------------------------------
 template <int FMT>
 __device__ __forceinline__ u32x4 cast16(const u32x4 &p, const u32x4 &q, float s, bool fast) {
@@ -47,6 +47,8 @@ __device__ __forceinline__ uint32_t amax_vec(uint32_t acc, const u32x4 &v) {
     return amax_pk(acc, v.w);
 }
 
+constexpr int kCastMaxBlocks = 2048;
+
 template <int FMT>
 __global__ __launch_bounds__(256) void k_cast_amax(const uint16_t *__restrict__ x, int64_t n,
                                                    const float *__restrict__ scale_p,
@@ -58,23 +60,27 @@ __global__ __launch_bounds__(256) void k_cast_amax(const uint16_t *__restrict__ 
     const float s = *scale_p;
     const bool plain = scale_is_plain(s);
     uint32_t am = 0;
-    const int64_t nvec = n >> 5;                       // 32-element groups
+    const int64_t nvec = n >> 4;                       // 16-element groups
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (v << 5));
-        const u32x4 p0 = __builtin_nontemporal_load(src), q0 = __builtin_nontemporal_load(src + 1);
-        const u32x4 p1 = __builtin_nontemporal_load(src + 2), q1 = __builtin_nontemporal_load(src + 3);
-        uint32_t tam = amax_vec(amax_vec(amax_vec(amax_vec(0u, p0), q0), p1), q1);
+    for (int64_t v0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v0 < nvec; v0 += 2 * stride) {
+        const int64_t v1 = v0 + stride;
+        const bool has1 = v1 < nvec;
+        const u32x4 *s0 = reinterpret_cast<const u32x4 *>(x + (v0 << 4));
+        const u32x4 p0 = __builtin_nontemporal_load(s0), q0 = __builtin_nontemporal_load(s0 + 1);
+        u32x4 p1 = {0u, 0u, 0u, 0u}, q1 = {0u, 0u, 0u, 0u};
+        if (has1) {
+            const u32x4 *s1 = reinterpret_cast<const u32x4 *>(x + (v1 << 4));
+            p1 = __builtin_nontemporal_load(s1);
+            q1 = __builtin_nontemporal_load(s1 + 1);
+        }
+        const uint32_t tam = amax_vec(amax_vec(amax_vec(amax_vec(0u, p0), q0), p1), q1);
         const bool fast = plain && amax_unpack(tam) < 0x7F80u;
-        const u32x4 o0 = cast16<FMT>(p0, q0, s, fast);
-        const u32x4 o1 = cast16<FMT>(p1, q1, s, fast);
         am = amax_pk(am, tam);
-        u32x4 *dst = reinterpret_cast<u32x4 *>(out + (v << 5));
-        __builtin_nontemporal_store(o0, dst);
-        __builtin_nontemporal_store(o1, dst + 1);
+        __builtin_nontemporal_store(cast16<FMT>(p0, q0, s, fast), reinterpret_cast<u32x4 *>(out + (v0 << 4)));
+        if (has1) __builtin_nontemporal_store(cast16<FMT>(p1, q1, s, fast), reinterpret_cast<u32x4 *>(out + (v1 << 4)));
     }
     // remainder
-    for (int64_t i = (nvec << 5) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    for (int64_t i = (nvec << 4) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
         uint32_t w = x[i];
         am = amax_pk(am, w);
         out[i] = (uint8_t)encode_exact<FMT>(bf16_lo(w) * s);
@@ -322,10 +328,10 @@ __global__ __launch_bounds__(256) void k_dbias_reduce(const float *__restrict__ 
 hipError_t launch_cast_amax(const uint16_t *x, int64_t n, const float *scale, int fmt, uint8_t *out,
                             float *sinv_out, float *amax_slot, const float *noop, hipStream_t st) {
     if (n == 0) return hipSuccess;
-    int64_t nvec = n >> 5;
-    int64_t blocks = (nvec + 255) / 256;
+    int64_t nvec = n >> 4;
+    int64_t blocks = (nvec + 511) / 512;
     if (blocks < 1) blocks = 1;
-    if (blocks > 256 * 16) blocks = 256 * 16;  // grid-stride beyond 16 blocks per CU
+    if (blocks > kCastMaxBlocks) blocks = kCastMaxBlocks;  // grid-stride beyond that
     if (fmt == kE4M3)
         k_cast_amax<kE4M3><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(x, n, scale, out, sinv_out, amax_slot, noop);
     else

@@ -97,8 +97,15 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *red) {
 // Fold a bfloat16 magnitude bit pattern (0..0xFFFF without sign) into a float32 amax slot.
 // The slot holds a non-negative float or NaN; for those, unsigned order of the bit patterns is
 // the numeric order (with NaN above +inf), so an integer atomic max is exact and order free.
+// The slot only grows while casts run, so a plain read that already shows a value at least as
+// large proves the atomic would change nothing: skipping it keeps thousands of blocks from
+// serialising on one address.
 __device__ __forceinline__ void fold_amax(float *slot, uint32_t bf16_mag) {
-    if (slot != nullptr && bf16_mag != 0u) atomicMax(reinterpret_cast<unsigned int *>(slot), bf16_mag << 16);
+    if (slot == nullptr || bf16_mag == 0u) return;
+    unsigned int *u = reinterpret_cast<unsigned int *>(slot);
+    const unsigned int bits = bf16_mag << 16;
+    if (__hip_atomic_load(u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= bits) return;
+    atomicMax(u, bits);
 }
 
 }  // namespace fp8ds
