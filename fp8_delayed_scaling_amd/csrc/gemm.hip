@@ -13,7 +13,7 @@
 // Blocks are remapped so that each XCD (blocks are dealt round-robin to the 8 XCDs) works on a
 // contiguous range of tiles, walked in groups of kGroupM tile-rows for L2 reuse.  Epilogue:
 // acc * a_scale_inv * b_scale_inv + bias in float32, rounded to bfloat16 (nearest even) or stored
-// as float32.  Ragged M / N are handled by clamping the rows that are loaded and masking the
+// as float32 (the pipelined kernel stages it through LDS and writes 16-byte row segments).  Ragged M / N are handled by clamping the rows that are loaded and masking the
 // stores.  No split-K: every output element is one fixed sequence of MFMAs over K in the same
 // K order in both kernels, whatever tile it falls in.
 //
@@ -98,6 +98,120 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], const float 
                         reinterpret_cast<float *>(D)[(int64_t)row * ldd + col] = v;
                 }
             }
+        }
+    }
+}
+
+// Epilogue of the pipelined kernel, whose MFMAs take B as the first operand: there lane l holds
+// D[row0 + 32 i + l % 32][col0 + 32 j + 8 (e / 4) + 4 (l / 32) + e % 4] in element e of acc[i][j]
+// (the products and their summation order are the same as with A first).  Each wave scales, adds
+// the bias and rounds its 128 x 128 sub-tile into its own 32 KB of LDS, then writes whole rows
+// with 16-byte streaming (nontemporal) stores.  bf16: one pass, row r at r * 256, 8-byte slot s
+// (columns 4 s .. 4 s + 3) stored at slot s ^ (r & 31).  float32: two passes of 64 rows, row r at
+// r * 512, 16-byte slot s at s ^ (r & 31).  Where D or ldd is not 16-byte aligned, or at the
+// ragged right edge, the elements are stored one by one.
+template <int OUT>
+__device__ __forceinline__ void epilogue_staged(const f32x16 (&acc)[4][4], const float *__restrict__ a_sinv,
+                                                const float *__restrict__ b_sinv, const uint16_t *__restrict__ bias,
+                                                void *__restrict__ D, int64_t ldd, int M, int N, int row0, int col0,
+                                                int lane, uint8_t *wlds) {
+    const int frow = lane & 31, fhalf = lane >> 5;
+    const float sa = *a_sinv, sb = *b_sinv;
+    const bool vec_ok = ((reinterpret_cast<uintptr_t>(D) & 15u) == 0) && (ldd % (OUT == 0 ? 8 : 4) == 0);
+    // bias of the 16 columns this lane holds in column block j
+    auto load_bias = [&](int j, float (&bv)[4][4]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int col = col0 + j * 32 + q * 8 + fhalf * 4 + u;
+                bv[q][u] = (bias != nullptr && col < N) ? __uint_as_float((uint32_t)bias[col] << 16) : 0.f;
+            }
+    };
+    if constexpr (OUT == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float bv[4][4];
+            load_bias(j, bv);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = i * 32 + frow, sl = j * 8 + q * 2 + fhalf;
+                    float v[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) v[u] = acc[i][j][q * 4 + u] * sa * sb + bv[q][u];
+                    const u32x2 pk = {(uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16),
+                                      (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16)};
+                    *reinterpret_cast<u32x2 *>(wlds + r * 256 + ((sl ^ (r & 31)) << 3)) = pk;
+                }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        // 16-byte chunk ch of row r = slots 2 ch, 2 ch + 1, stored at (2 ch) ^ x and (2 ch + 1) ^ x
+        // with x = r & 31: one aligned 16-byte read at (2 ch) ^ (x & ~1), halves swapped if x is odd.
+#pragma unroll
+        for (int pq = 0; pq < 32; ++pq) {
+            const int r = pq * 4 + (lane >> 4), ch = lane & 15;
+            const int x = r & 31;
+            u32x4 v = *reinterpret_cast<const u32x4 *>(wlds + r * 256 + (((2 * ch) ^ (x & ~1)) << 3));
+            if (x & 1) v = v.zwxy;
+            const int row = row0 + r, col = col0 + ch * 8;
+            if (row < M && col < N) {
+                uint16_t *dst = reinterpret_cast<uint16_t *>(D) + (int64_t)row * ldd + col;
+                if (vec_ok && col + 7 < N) {
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst));
+                } else {
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        if (col + u < N) dst[u] = (uint16_t)(w[u >> 1] >> (16 * (u & 1)));
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float bv[4][4];
+                load_bias(j, bv);
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int i = h * 2 + ii;
+                        const int r = ii * 32 + frow, sl = j * 8 + q * 2 + fhalf;
+                        u32x4 pk;
+                        pk.x = __float_as_uint(acc[i][j][q * 4 + 0] * sa * sb + bv[q][0]);
+                        pk.y = __float_as_uint(acc[i][j][q * 4 + 1] * sa * sb + bv[q][1]);
+                        pk.z = __float_as_uint(acc[i][j][q * 4 + 2] * sa * sb + bv[q][2]);
+                        pk.w = __float_as_uint(acc[i][j][q * 4 + 3] * sa * sb + bv[q][3]);
+                        *reinterpret_cast<u32x4 *>(wlds + r * 512 + ((sl ^ (r & 31)) << 4)) = pk;
+                    }
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int pq = 0; pq < 32; ++pq) {
+                const int r = pq * 2 + (lane >> 5), ch = lane & 31;
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(wlds + r * 512 + ((ch ^ (r & 31)) << 4));
+                const int row = row0 + h * 64 + r, col = col0 + ch * 4;
+                if (row < M && col < N) {
+                    float *dst = reinterpret_cast<float *>(D) + (int64_t)row * ldd + col;
+                    if (vec_ok && col + 3 < N) {
+                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst));
+                    } else {
+                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            if (col + u < N) dst[u] = __uint_as_float(w[u]);
+                    }
+                }
+            }
+            // the second pass overwrites what this pass read
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
         }
     }
 }
@@ -316,7 +430,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias_pipe(const uint8_t *_
 #define FP8DS_MFMA(CA, CB)                                                                                \
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                         \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                         \
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(CA[i], CB[j], acc[i][j], FA, FB, 0, 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(CB[j], CA[i], acc[i][j], FB, FA, 0, 0, 0, 0);
     // One slice: wait for slice kt+1, barrier, issue slice kt+3 into the stage slice kt-1 used,
     // prefetch slice kt+1's fragments, run slice kt's 16 MFMAs (interleaved by the scheduler).
 #define FP8DS_STEP(kt, NXT1, ISS, CA, CB, NA, NB)                                                         \
@@ -373,7 +487,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias_pipe(const uint8_t *_
 #undef FP8DS_FRAGS
 #undef FP8DS_MFMA
 #undef FP8DS_STEP
-    epilogue<OUT>(acc, a_sinv, b_sinv, bias, D, ldd, M, N, m0 + wm * 128, n0 + wn * 128, lane);
+    __syncthreads();   // every wave is done reading the operand stages
+    uint8_t *wl = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
+    epilogue_staged<OUT>(acc, a_sinv, b_sinv, bias, D, ldd, M, N, m0 + wm * 128, n0 + wn * 128, lane, wl);
 }
 
 // D = bias broadcast (K == 0): no products at all.

@@ -219,3 +219,26 @@ def test_empty_inputs_launch_nothing():
     F.fp8_dbias_cast_transpose(x2, scalar(1.0), F.E5M2, None, None, db, None)
     torch.cuda.synchronize()
     assert sinv.item() == -1.0 and torch.all(db == 0.0)
+
+
+@pytest.mark.parametrize("fmt", [F.E4M3, F.E5M2])
+def test_cast_exhaustive_bf16_patterns_times_scales(fmt):
+    """All 65536 bfloat16 bit patterns (every sign, exponent and mantissa, subnormals, +-0,
+    +-inf and NaNs) times 40 scales from 2^-30 to 2^30 plus odd values: the cast's whole input
+    domain for each scale, through both the 1-D cast and the cast+transpose, bit-exact."""
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    scales = [float(v) for v in 2.0 ** np.linspace(-30, 30, 33)] + [1.0, 3.0, 0.1, 112.0, 448.0, 57344.0, 1e-38]
+    x2 = bf16_dev(allb.reshape(256, 256))
+    x1 = bf16_dev(allb)
+    for sc in scales:
+        out = torch.empty(65536, dtype=torch.uint8, device=DEV)
+        F.fp8_cast_amax(x1, scalar(sc), fmt, out)
+        q = torch.empty((256, 256), dtype=torch.uint8, device=DEV)
+        qt = torch.empty((256, 256), dtype=torch.uint8, device=DEV)
+        F.fp8_cast_transpose(x2, scalar(sc), fmt, q, qt)
+        torch.cuda.synchronize()
+        ref, _, _ = oracle.cast_amax(allb, sc, fmt)
+        got = u8_host(out)
+        assert np.array_equal(got, ref), (sc, np.nonzero(got != ref)[0][:5])
+        assert np.array_equal(u8_host(q).reshape(-1), ref), sc
+        assert np.array_equal(u8_host(qt), ref.reshape(256, 256).T), sc
