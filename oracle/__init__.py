@@ -76,6 +76,8 @@ def lib():
         L.orc_cast_amax.argtypes = [P, i64, f32, i32, P, P]
         L.orc_cast_transpose.argtypes = [P, i64, i64, f32, i32, P, P, P]
         L.orc_dbias.argtypes = [P, i64, i64, P]
+        L.orc_fp8_transpose.argtypes = [P, i64, i64, P]
+        L.orc_cast_f32_amax.argtypes = [P, i64, f32, i32, P, P]
         L.orc_scale_inv.argtypes = [f32]
         L.orc_scale_inv.restype = f32
         L.orc_scale_update.argtypes = [P, i64, i64, P, P, P, ctypes.c_int32]
@@ -83,7 +85,7 @@ def lib():
         L.orc_gemm_bias_scalar.argtypes = [P, i32, f32, i64, P, i32, f32, i64, P, i64, i64, i64, P, i64]
         for fn in ("orc_fp8_encode_n", "orc_fp8_encode_search_n", "orc_fp8_decode_n", "orc_cast_amax",
                    "orc_cast_transpose", "orc_dbias", "orc_scale_update", "orc_dequant",
-                   "orc_gemm_bias_scalar"):
+                   "orc_gemm_bias_scalar", "orc_fp8_transpose", "orc_cast_f32_amax"):
             getattr(L, fn).restype = None
         _lib = L
     return _lib
@@ -163,6 +165,34 @@ def cast_transpose(x_bf16, scale: float, fmt: int, amax_in: float = 0.0):
     return out, out_t, amax[0], scale_inv(scale)
 
 
+def fp8_transpose(codes, noop: bool = False, out_t_prev=None) -> np.ndarray:
+    """Transpose cache of an existing 2-D FP8 tensor: ``[C, R]`` codes, moved not re-encoded.
+
+    With ``noop`` set the cache is left as it was: ``out_t_prev`` is returned unchanged (the
+    weight-caching flag of [CG], "noop_flag in transpose").
+    """
+    c = _c(codes, np.uint8)
+    if c.ndim != 2:
+        raise ValueError("fp8_transpose takes a 2-D tensor")
+    R, C = c.shape
+    if noop:
+        if out_t_prev is None:
+            raise ValueError("noop needs the previous cache")
+        return np.array(out_t_prev, copy=True)
+    out_t = np.empty((C, R), dtype=np.uint8)
+    lib().orc_fp8_transpose(_p(c), R, C, _p(out_t))
+    return out_t
+
+
+def cast_f32_amax(x_f32, scale: float, fmt: int, amax_in: float = 0.0):
+    """``(codes, amax, scale_inv)`` of a float32 tensor cast with ``scale`` (amax of |x|)."""
+    x = _c(x_f32, np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    amax = np.array([amax_in], dtype=np.float32)
+    lib().orc_cast_f32_amax(_p(x), x.size, np.float32(scale), fmt, _p(out), _p(amax))
+    return out, amax[0], scale_inv(scale)
+
+
 def dbias(dy_bf16) -> np.ndarray:
     """float64 column sums of a 2-D bfloat16 tensor."""
     x = _c(dy_bf16, np.uint16)
@@ -226,6 +256,20 @@ def gemm_bias(A, fa: int, a_sinv: float, B, fb: int, b_sinv: float, bias_bf16=No
         raise ValueError("A and B must share K")
     acc = Ad @ Bd.T
     return acc * np.float64(np.float32(a_sinv)) * np.float64(np.float32(b_sinv)) + _bias_f64(bias_bf16, Bd.shape[0])[None, :]
+
+
+def gemm_bias_fp8(A, fa: int, a_sinv: float, B, fb: int, b_sinv: float, bias_bf16, d_fmt: int,
+                  d_scale: float, amax_in: float = 0.0):
+    """FP8-output GEMM ([CG] transpose-cache thread: fp8_gemm(..., out=dx._data)).
+
+    The output value D is the plain GEMM+bias rounded once to float32 (the GEMM's accumulate
+    and epilogue type); D is then cast like any float32 tensor with the output's own scale:
+    ``codes = enc(D * d_scale)``, ``amax = max |D|`` folded into ``amax_in``, and the output's
+    private inverse scale 1/d_scale.  Returns ``(codes, amax, scale_inv, D_f32)``.
+    """
+    D = gemm_bias(A, fa, a_sinv, B, fb, b_sinv, bias_bf16).astype(np.float32)
+    codes, amax, sinv = cast_f32_amax(D, d_scale, d_fmt, amax_in)
+    return codes, amax, sinv, D
 
 
 def gemm_bias_scalar(A, fa, a_sinv, B, fb, b_sinv, bias_bf16=None) -> np.ndarray:

@@ -203,6 +203,37 @@ void orc_cast_transpose(const uint16_t *x, int64_t rows, int64_t cols, float sca
 }
 
 /*
+ * Transpose of an FP8 tensor that already exists: the lazy fill of a Float8Tensor's transpose
+ * cache ([WS] "grown in scope" first bullet: transpose_2d(cache=True) and lazy transpose
+ * caching; [CG] transpose-cache thread: dy.transpose() of an FP8 dy that carries no cached
+ * transpose).  The codes are moved, never re-encoded: in is [rows, cols] row-major and out_t
+ * is [cols, rows] with out_t[j][i] = in[i][j].
+ */
+void orc_fp8_transpose(const uint8_t *in, int64_t rows, int64_t cols, uint8_t *out_t)
+{
+    for (int64_t j = 0; j < cols; ++j)
+        for (int64_t i = 0; i < rows; ++i)
+            out_t[j * rows + i] = in[i * cols + j];
+}
+
+/*
+ * Cast of a float32 tensor with amax capture: the quantisation of an FP8 GEMM's output
+ * written straight into an FP8 tensor ([CG] transpose-cache thread: fp8_gemm(..., out=dx._data)
+ * in FP8Linear.backward).  Same two roundings as orc_cast_amax: y = x * scale in float32,
+ * then the saturating nearest-even encode; *amax_slot accumulates the largest |x|.
+ */
+void orc_cast_f32_amax(const float *x, int64_t n, float scale, int fmt, uint8_t *out, float *amax_slot)
+{
+    float amax = *amax_slot;
+    for (int64_t i = 0; i < n; ++i) {
+        float y = x[i] * scale;
+        out[i] = orc_fp8_encode(y, fmt);
+        amax = amax_fold(amax, x[i]);
+    }
+    *amax_slot = amax;
+}
+
+/*
  * Bias gradient: the column sum of dy ([CG] DbiasCastTranspose example: db = dy.sum(dim=0)),
  * taken from the bfloat16 dy before any cast, accumulated in float64.
  */

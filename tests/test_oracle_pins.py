@@ -401,3 +401,100 @@ def test_linear_fwd_bwd_shapes_and_definitions():
     assert np.allclose(g["dx"], (dyd @ wd).numpy(), rtol=1e-12, atol=1e-12)
     assert np.allclose(g["dw"], (dyd.T @ xd).numpy(), rtol=1e-12, atol=1e-12)
     assert np.allclose(g["dbias"], S.bf16_bits_to_f64(dy).sum(0), atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- FP8 transpose
+
+def _hex_block(rows):
+    return np.array([[int(v, 16) for v in r] for r in rows], dtype=np.uint8)
+
+
+def test_fp8_transpose_golden():
+    rows = _rows("fp8_transpose.txt")
+    cut = [r[0] for r in rows].index("out_t")
+    src, want = _hex_block(rows[1:cut]), _hex_block(rows[cut + 1:])
+    assert src.shape == (3, 5) and want.shape == (5, 3)
+    assert np.array_equal(oracle.fp8_transpose(src), want)
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (1, 7), (9, 1), (17, 33), (64, 48)])
+def test_fp8_transpose_brute_force_and_involution(shape):
+    R, C = shape
+    rng = np.random.default_rng(R * 1000 + C)
+    x = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    t = oracle.fp8_transpose(x)
+    assert t.shape == (C, R)
+    for i in range(R):
+        for j in range(C):
+            assert t[j, i] == x[i, j]
+    assert np.array_equal(oracle.fp8_transpose(t), x)
+
+
+def test_fp8_transpose_empty_and_noop():
+    assert oracle.fp8_transpose(np.zeros((0, 5), np.uint8)).shape == (5, 0)
+    x = np.arange(12, dtype=np.uint8).reshape(3, 4)
+    stale = np.full((4, 3), 0xAB, dtype=np.uint8)
+    assert np.array_equal(oracle.fp8_transpose(x, noop=True, out_t_prev=stale), stale)
+    with pytest.raises(ValueError):
+        oracle.fp8_transpose(x, noop=True)
+
+
+def test_cast_transpose_is_cast_then_transpose():
+    x = S.normal_bf16(S.seed_for(9, 0), (40, 24), 1.0)
+    q, qt, _, _ = oracle.cast_transpose(x, 3.0, oracle.E4M3)
+    assert np.array_equal(oracle.fp8_transpose(q), qt)
+
+
+# ----------------------------------------------------------------------------- FP8-output GEMM
+
+def test_cast_f32_amax_matches_bf16_cast_on_bf16_values():
+    # float32 inputs that are exactly bfloat16 values (every pattern, incl. inf, NaN, -0) must
+    # cast exactly like the bfloat16 cast, whose encoder and amax are pinned above.
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    xf = (allb.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    for fmt in (oracle.E4M3, oracle.E5M2):
+        for s in (1.0, 0.0625, 3.0, 1e-30):
+            q1, a1, si1 = oracle.cast_amax(allb, s, fmt)
+            q2, a2, si2 = oracle.cast_f32_amax(xf, s, fmt)
+            assert np.array_equal(q1, q2)
+            assert _bits(a1) == _bits(a2) and _bits(si1) == _bits(si2)
+    finite = xf[np.isfinite(xf)]
+    _, a, _ = oracle.cast_f32_amax(finite, 1.0, oracle.E4M3)
+    assert a == np.abs(finite).max()
+
+
+def test_gemm_fp8_output_golden():
+    A = np.full((2, 64), 0x38, dtype=np.uint8)
+    B = np.full((4, 64), 0x38, dtype=np.uint8)
+    bias = np.array([0x0000, 0x3F00, 0xC1A0, 0x4396], dtype=np.uint16)
+    rows = _rows("fp8_gemm_fp8out.txt")
+    assert len(rows) == 5
+    for fmt, sbits, abits, c0, c1, c2, c3, amax_bits, sinv_bits in rows:
+        codes, amax, sinv, D = oracle.gemm_bias_fp8(A, oracle.E4M3, 0.5, B, oracle.E4M3, 0.25, bias, FMT[fmt],
+                                                    _f32(sbits)[0], _f32(abits)[0])
+        assert np.array_equal(D, np.tile(np.array([8, 8.5, -12, 308], np.float32), (2, 1)))
+        want = np.array([int(c, 16) for c in (c0, c1, c2, c3)], dtype=np.uint8)
+        assert np.array_equal(codes, np.tile(want, (2, 1))), (fmt, sbits, codes)
+        assert _bits(amax) == int(amax_bits, 16) and _bits(sinv) == int(sinv_bits, 16)
+
+
+@pytest.mark.parametrize("fmt_out", [oracle.E4M3, oracle.E5M2])
+def test_gemm_fp8_output_identity_weight(fmt_out):
+    # B = identity (code 1.0 on the diagonal): D = dec(A) * sa * sb + bias exactly, with the
+    # A operand's row/column roles visible (A is not square).  Reference built from the pinned
+    # decode and the independent nearest-code search encoder.
+    M, K = 24, 32
+    rng = np.random.default_rng(7)
+    A = rng.integers(0, 256, size=(M, K), dtype=np.uint8)
+    A[(A & 0x7F) == 0x7F] = 0x3C                      # no NaN codes
+    B = np.zeros((K, K), dtype=np.uint8)
+    np.fill_diagonal(B, 0x38)
+    bias = S.normal_bf16(S.seed_for(9, 1), (K,), 0.5)
+    sa, sb, ds = np.float32(0.75), np.float32(2.0), np.float32(0.3)
+    codes, amax, sinv, D = oracle.gemm_bias_fp8(A, oracle.E4M3, sa, B, oracle.E4M3, sb, bias, fmt_out, ds)
+    bias_f = (bias.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    ref = (oracle.decode(A, oracle.E4M3) * np.float64(sa) * np.float64(sb) + bias_f[None, :]).astype(np.float32)
+    assert np.array_equal(D, ref)
+    assert np.array_equal(codes, oracle.encode_search(ref * ds, fmt_out))
+    assert amax == np.abs(ref).max()
+    assert _bits(sinv) == _bits(np.float32(1) / ds)
