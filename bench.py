@@ -16,6 +16,9 @@ Also reported (own timings, HIP events on the launch stream):
   * dbias+cast+transpose of dy [8192, 4096] and the T=3, L=1024 scale update;
   * the forward-only small layer ([128,256] x [256,256]): eager and graph-replay latency;
   * N-chunked GEMM+bias M=8192, K=N=12288 in 4 and 8 chunks on their own streams, as a graph;
+  * the lazy transpose-cache fill of the FP8 weight [18432, 12288], cold (GB/s);
+  * the FP8-output GEMM (E5M2 output, own scale, amax capture) at the dgrad shape, against the
+    bfloat16-output GEMM on the same operands;
   * the CPU oracle on a bounded sample of the same step (baseline only).
 """
 from __future__ import annotations
@@ -352,9 +355,9 @@ def extras(F, S, torch, np, dev, bf16):
 
     # N-chunked GEMM + bias, M=8192, K=N=12288, one stream per chunk, captured as one graph
     Mc, Kc, Nc = 8192, 12288, 12288
-    def codes(seed, rows):
+    def codes(seed, rows, cols=Kc):
         """Seeded finite E4M3 codes (exponent field even, so never the NaN code), mixed signs."""
-        c = torch.randint(0, 256, (rows, Kc), generator=torch.Generator().manual_seed(seed), dtype=torch.uint8)
+        c = torch.randint(0, 256, (rows, cols), generator=torch.Generator().manual_seed(seed), dtype=torch.uint8)
         return (c & 0xF7).to(dev)
 
     A8 = codes(7, Mc)
@@ -380,7 +383,35 @@ def extras(F, S, torch, np, dev, bf16):
         ms = _time_fn(torch, g.replay, 10)
         res[f"chunks{nch}_graph_tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
     out["chunked_gemm_8192x12288x12288"] = res
-    del A8, B8, D, flush
+    del A8, B8, D
+
+    # lazy transpose-cache fill of the FP8 weight [18432, 12288], cold (1 B read + 1 B written)
+    Rw, Cw = 18432, 12288
+    W8 = torch.randint(0, 256, (Rw, Cw), generator=torch.Generator().manual_seed(9), dtype=torch.uint8).to(dev)
+    W8t = torch.empty((Cw, Rw), **u8)
+    F.fp8_transpose(W8, W8t)
+    ms = cold_time(lambda: F.fp8_transpose(W8, W8t))
+    gbps = Rw * Cw * 2 / (ms * 1e-3) / 1e9
+    out["fp8_transpose_18432x12288_cold"] = {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
+                                              "frac_hbm": round(gbps * 1e9 / HBM_PEAK, 3)}
+    del W8, W8t
+
+    # GEMM writing an FP8 output with its own scale and amax capture, dgrad shape of the step
+    # (M=8192, N=12288, K=18432), against the bfloat16-output GEMM on the same operands
+    Mg, Ng, Kg = 8192, 12288, 18432
+    A8, B8 = codes(10, Mg, Kg), codes(11, Ng, Kg)
+    D8 = torch.empty((Mg, Ng), **u8)
+    Db = torch.empty((Mg, Ng), device=dev, dtype=torch.bfloat16)
+    ds, dsi, dam = torch.tensor([1.0 / 4096], **f32), torch.zeros(1, **f32), torch.zeros(1, **f32)
+    flop = 2.0 * Mg * Ng * Kg
+    F.fp8_gemm_bias_fp8(A8, 0, sa, B8, 0, sb, None, D8, F.E5M2, ds, dsi, dam)
+    F.fp8_gemm_bias(A8, 0, sa, B8, 0, sb, None, Db)
+    torch.cuda.synchronize()
+    t8 = _time_fn(torch, lambda: F.fp8_gemm_bias_fp8(A8, 0, sa, B8, 0, sb, None, D8, F.E5M2, ds, dsi, dam), 10)
+    tb = _time_fn(torch, lambda: F.fp8_gemm_bias(A8, 0, sa, B8, 0, sb, None, Db), 10)
+    out["fp8_out_gemm_8192x12288x18432"] = {"fp8_out_tflops": round(flop / (t8 * 1e-3) / 1e12, 1),
+                                             "bf16_out_tflops": round(flop / (tb * 1e-3) / 1e12, 1)}
+    del A8, B8, D8, Db, flush
     torch.cuda.empty_cache()
     return out
 

@@ -22,7 +22,8 @@ __all__ = [
     "E4M3", "E5M2", "OUT_BF16", "OUT_FP32", "Fp8dsError", "lib", "library_path",
     "fp8ds_status_string", "fp8ds_version",
     "fp8_cast_amax", "fp8_cast_transpose", "fp8_dbias_workspace_bytes", "fp8_dbias_cast_transpose",
-    "fp8_scale_update", "fp8_gemm_bias", "fp8_gemm_bias_chunked", "fp8_linear_fwd", "fp8_linear_bwd",
+    "fp8_scale_update", "fp8_gemm_bias", "fp8_gemm_bias_chunked", "fp8_gemm_bias_fp8", "fp8_transpose",
+    "fp8_linear_fwd", "fp8_linear_bwd",
 ]
 
 E4M3 = 0
@@ -59,6 +60,8 @@ _SIGS = {
     "fp8_scale_update": ([P, I64, I64, P, P, P, I32, P], INT),
     "fp8_gemm_bias": ([P, INT, P, I64, P, INT, P, I64, P, P, I64, INT, I64, I64, I64, P], INT),
     "fp8_gemm_bias_chunked": ([P, INT, P, I64, P, INT, P, I64, P, P, I64, INT, I64, I64, I64, INT, P, P], INT),
+    "fp8_gemm_bias_fp8": ([P, INT, P, I64, P, INT, P, I64, P, P, I64, INT, P, P, P, I64, I64, I64, P], INT),
+    "fp8_transpose": ([P, I64, I64, P, P, P], INT),
     "fp8_linear_fwd": ([P, P, P, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, P, P, P], INT),
     "fp8_linear_bwd": ([P, I64, I64, I64, P, P, P, P, P, P, P, SZ, P, P, P, P, P, P, INT, P], INT),
 }
@@ -198,7 +201,7 @@ def _gemm_args(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D):
     if tuple(D.shape) != (M, N):
         raise ValueError("D must be [M, N]")
     for t, nm in ((A, "A"), (B, "B"), (D, "D")):
-        if t.stride(1) != 1:
+        if t.numel() and t.stride(1) != 1:
             raise ValueError(f"{nm} rows must be contiguous")
     return (_ptr(A), int(fa), _ptr(a_scale_inv), A.stride(0), _ptr(B), int(fb), _ptr(b_scale_inv), B.stride(0),
             _ptr(bias), _ptr(D), D.stride(0), _out_dtype(D), M, N, K)
@@ -207,6 +210,39 @@ def _gemm_args(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D):
 def fp8_gemm_bias(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D, stream=None):
     """D = (A B^T) * a_scale_inv * b_scale_inv + bias, A [M, K] and B [N, K] FP8 codes."""
     _check(lib().fp8_gemm_bias(*_gemm_args(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D), _stream(stream)))
+
+
+def fp8_gemm_bias_fp8(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D, d_fmt, d_scale, d_scale_inv_out=None,
+                      d_amax_slot=None, stream=None):
+    """FP8-output GEMM: D = codes of ((A B^T) * a_scale_inv * b_scale_inv + bias) * d_scale, with the
+    output's amax folded into ``d_amax_slot`` and 1/d_scale written to ``d_scale_inv_out``."""
+    _want(D, (torch.uint8,), "D", contiguous=False)
+    _want(A, (torch.uint8,), "A", contiguous=False)
+    _want(B, (torch.uint8,), "B", contiguous=False)
+    _want(bias, _BF16, "bias")
+    M, K = A.shape
+    N, K2 = B.shape
+    if K != K2:
+        raise ValueError("A and B must share K")
+    if tuple(D.shape) != (M, N):
+        raise ValueError("D must be [M, N]")
+    for t, nm in ((A, "A"), (B, "B"), (D, "D")):
+        if t.numel() and t.stride(1) != 1:
+            raise ValueError(f"{nm} rows must be contiguous")
+    _check(lib().fp8_gemm_bias_fp8(_ptr(A), int(fa), _ptr(a_scale_inv), A.stride(0), _ptr(B), int(fb),
+                                   _ptr(b_scale_inv), B.stride(0), _ptr(bias), _ptr(D), D.stride(0), int(d_fmt),
+                                   _ptr(d_scale), _ptr(d_scale_inv_out), _ptr(d_amax_slot), M, N, K,
+                                   _stream(stream)))
+
+
+def fp8_transpose(x8, out_t, noop=None, stream=None):
+    """Transpose cache of an existing FP8 tensor: out_t [C, R] = x8 [R, C]^T (codes copied)."""
+    _want(x8, (torch.uint8,), "x8")
+    _want(out_t, (torch.uint8,), "out_t")
+    R, C = x8.shape
+    if tuple(out_t.shape) != (C, R):
+        raise ValueError("out_t must be [C, R]")
+    _check(lib().fp8_transpose(_ptr(x8), R, C, _ptr(out_t), _ptr(noop), _stream(stream)))
 
 
 def fp8_gemm_bias_chunked(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D, n_chunks: int,

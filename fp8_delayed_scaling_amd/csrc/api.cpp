@@ -20,6 +20,9 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 inline bool valid_fmt(int f) { return f == FP8DS_E4M3 || f == FP8DS_E5M2; }
 inline bool valid_out(int d) { return d == FP8DS_OUT_BF16 || d == FP8DS_OUT_FP32; }
+// Output codes of the GEMM launcher: the two public dtypes, then FP8 output in each format.
+constexpr int kOutE4M3 = 2, kOutE5M2 = 3;
+inline int64_t out_esize(int d) { return d == FP8DS_OUT_BF16 ? 2 : d == FP8DS_OUT_FP32 ? 4 : 1; }
 inline int hip_status(hipError_t e) { return e == hipSuccess ? FP8DS_OK : FP8DS_ERR_HIP; }
 
 // rows * cols fits comfortably in int64 (and in the kernels' index arithmetic)
@@ -41,7 +44,7 @@ int check_cast_common(const uint16_t *x, const float *scale, int fmt, const uint
 int check_gemm(const uint8_t *A, int fa, const float *a_sinv, int64_t lda, const uint8_t *B, int fb,
                const float *b_sinv, int64_t ldb, const uint16_t *bias, const void *D, int64_t ldd, int out_dtype,
                int64_t M, int64_t N, int64_t K) {
-    if (!valid_fmt(fa) || !valid_fmt(fb) || !valid_out(out_dtype)) return FP8DS_ERR_FORMAT;
+    if (!valid_fmt(fa) || !valid_fmt(fb) || out_dtype < 0 || out_dtype > kOutE5M2) return FP8DS_ERR_FORMAT;
     if (M < 0 || N < 0 || K < 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return FP8DS_ERR_SHAPE;
     if (K % 16 != 0) return FP8DS_ERR_SHAPE;
     if (((M + 255) / 256) * ((N + 255) / 256) > INT_MAX) return FP8DS_ERR_SHAPE;
@@ -50,7 +53,7 @@ int check_gemm(const uint8_t *A, int fa, const float *a_sinv, int64_t lda, const
     if (K > 0 && (A == nullptr || B == nullptr || a_sinv == nullptr || b_sinv == nullptr)) return FP8DS_ERR_NULL;
     if (K > 0 && (lda < K || ldb < K)) return FP8DS_ERR_SHAPE;
     if (ldd < N) return FP8DS_ERR_SHAPE;
-    const uintptr_t esize = out_dtype == FP8DS_OUT_BF16 ? 2 : 4;
+    const uintptr_t esize = (uintptr_t)out_esize(out_dtype);
     if ((reinterpret_cast<uintptr_t>(D) & (esize - 1)) != 0) return FP8DS_ERR_ALIGN;
     if (K > 0 && (lda % 16 != 0 || ldb % 16 != 0 || !aligned16(A) || !aligned16(B))) return FP8DS_ERR_ALIGN;
     if ((a_sinv && !aligned4(a_sinv)) || (b_sinv && !aligned4(b_sinv))) return FP8DS_ERR_ALIGN;
@@ -171,10 +174,36 @@ int fp8_scale_update(float *amax_history, int64_t L, int64_t T, float *scale, fl
 int fp8_gemm_bias(const uint8_t *A, int fa, const float *a_scale_inv, int64_t lda, const uint8_t *B, int fb,
                   const float *b_scale_inv, int64_t ldb, const uint16_t *bias, void *D, int64_t ldd, int out_dtype,
                   int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    if (!valid_out(out_dtype)) return FP8DS_ERR_FORMAT;
     int st = check_gemm(A, fa, a_scale_inv, lda, B, fb, b_scale_inv, ldb, bias, D, ldd, out_dtype, M, N, K);
     if (st != FP8DS_OK) return st;
     return hip_status(fp8ds::launch_gemm_bias(A, fa, a_scale_inv, lda, B, fb, b_scale_inv, ldb, bias, D, ldd,
-                                              out_dtype, M, N, K, stream));
+                                              out_dtype, M, N, K, nullptr, nullptr, nullptr, stream));
+}
+
+int fp8_gemm_bias_fp8(const uint8_t *A, int fa, const float *a_scale_inv, int64_t lda, const uint8_t *B, int fb,
+                      const float *b_scale_inv, int64_t ldb, const uint16_t *bias, uint8_t *D, int64_t ldd,
+                      int d_fmt, const float *d_scale, float *d_scale_inv_out, float *d_amax_slot, int64_t M,
+                      int64_t N, int64_t K, hipStream_t stream) {
+    if (!valid_fmt(d_fmt)) return FP8DS_ERR_FORMAT;
+    if (d_scale == nullptr) return FP8DS_ERR_NULL;
+    if (!aligned4(d_scale) || (d_scale_inv_out && !aligned4(d_scale_inv_out)) || (d_amax_slot && !aligned4(d_amax_slot)))
+        return FP8DS_ERR_ALIGN;
+    const int out = d_fmt == FP8DS_E4M3 ? kOutE4M3 : kOutE5M2;
+    int st = check_gemm(A, fa, a_scale_inv, lda, B, fb, b_scale_inv, ldb, bias, D, ldd, out, M, N, K);
+    if (st != FP8DS_OK) return st;
+    return hip_status(fp8ds::launch_gemm_bias(A, fa, a_scale_inv, lda, B, fb, b_scale_inv, ldb, bias, D, ldd, out,
+                                              M, N, K, d_scale, d_scale_inv_out, d_amax_slot, stream));
+}
+
+int fp8_transpose(const uint8_t *in, int64_t rows, int64_t cols, uint8_t *out_t, const float *noop,
+                  hipStream_t stream) {
+    if (!size_ok(rows, cols)) return FP8DS_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return FP8DS_OK;
+    if (((rows + 255) / 256) * ((cols + 255) / 256) > INT_MAX) return FP8DS_ERR_SHAPE;
+    if (in == nullptr || out_t == nullptr) return FP8DS_ERR_NULL;
+    if (noop && !aligned4(noop)) return FP8DS_ERR_ALIGN;
+    return hip_status(fp8ds::launch_fp8_transpose(in, rows, cols, out_t, noop, stream));
 }
 
 int fp8_gemm_bias_chunked(const uint8_t *A, int fa, const float *a_scale_inv, int64_t lda, const uint8_t *B, int fb,
@@ -182,6 +211,7 @@ int fp8_gemm_bias_chunked(const uint8_t *A, int fa, const float *a_scale_inv, in
                           int out_dtype, int64_t M, int64_t N, int64_t K, int n_chunks,
                           const hipStream_t *chunk_streams, hipStream_t stream) {
     if (n_chunks < 1 || n_chunks > kMaxChunks) return FP8DS_ERR_ARG;
+    if (!valid_out(out_dtype)) return FP8DS_ERR_FORMAT;
     int st = check_gemm(A, fa, a_scale_inv, lda, B, fb, b_scale_inv, ldb, bias, D, ldd, out_dtype, M, N, K);
     if (st != FP8DS_OK) return st;
     if (M == 0 || N == 0) return FP8DS_OK;
@@ -202,7 +232,8 @@ int fp8_gemm_bias_chunked(const uint8_t *A, int fa, const float *a_scale_inv, in
         if (chunk_streams != nullptr && hipStreamWaitEvent(s, ev->fork, 0) != hipSuccess) return FP8DS_ERR_HIP;
         hipError_t e = fp8ds::launch_gemm_bias(A, fa, a_scale_inv, lda, B + c0 * ldb, fb, b_scale_inv, ldb,
                                                bias != nullptr ? bias + c0 : nullptr,
-                                               static_cast<uint8_t *>(D) + c0 * esize, ldd, out_dtype, M, cn, K, s);
+                                               static_cast<uint8_t *>(D) + c0 * esize, ldd, out_dtype, M, cn, K,
+                                               nullptr, nullptr, nullptr, s);
         if (e != hipSuccess) return FP8DS_ERR_HIP;
         if (chunk_streams != nullptr) {
             if (hipEventRecord(ev->join[c], s) != hipSuccess) return FP8DS_ERR_HIP;
@@ -244,7 +275,7 @@ int fp8_linear_fwd(const uint16_t *x, const uint16_t *w, const uint16_t *bias, i
         if (e != hipSuccess) return FP8DS_ERR_HIP;
     }
     return hip_status(fp8ds::launch_gemm_bias(x8, FP8DS_E4M3, x_scale_inv, K, w8, FP8DS_E4M3, w_scale_inv, K, bias,
-                                              y, N, FP8DS_OUT_BF16, M, N, K, stream));
+                                              y, N, FP8DS_OUT_BF16, M, N, K, nullptr, nullptr, nullptr, stream));
 }
 
 int fp8_linear_bwd(const uint16_t *dy, int64_t M, int64_t N, int64_t K, const float *dy_scale, float *dy_amax,
@@ -279,10 +310,10 @@ int fp8_linear_bwd(const uint16_t *dy, int64_t M, int64_t N, int64_t K, const fl
                                                       dy_amax, nullptr, stream);
     if (e != hipSuccess) return FP8DS_ERR_HIP;
     e = fp8ds::launch_gemm_bias(dy8, FP8DS_E5M2, dy_scale_inv, N, w8_t, FP8DS_E4M3, w_scale_inv, N, nullptr, dx, K,
-                                FP8DS_OUT_BF16, M, K, N, stream);
+                                FP8DS_OUT_BF16, M, K, N, nullptr, nullptr, nullptr, stream);
     if (e != hipSuccess) return FP8DS_ERR_HIP;
     return hip_status(fp8ds::launch_gemm_bias(dy8_t, FP8DS_E5M2, dy_scale_inv, M, x8_t, FP8DS_E4M3, x_scale_inv, M,
-                                              nullptr, dw, K, dw_dtype, N, K, M, stream));
+                                              nullptr, dw, K, dw_dtype, N, K, M, nullptr, nullptr, nullptr, stream));
 }
 
 }  // extern "C"

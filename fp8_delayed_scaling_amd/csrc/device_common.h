@@ -100,12 +100,22 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *red) {
 // The slot only grows while casts run, so a plain read that already shows a value at least as
 // large proves the atomic would change nothing: skipping it keeps thousands of blocks from
 // serialising on one address.
-__device__ __forceinline__ void fold_amax(float *slot, uint32_t bf16_mag) {
-    if (slot == nullptr || bf16_mag == 0u) return;
+__device__ __forceinline__ void fold_amax_bits(float *slot, uint32_t f32_mag) {
+    if (slot == nullptr || f32_mag == 0u) return;
     unsigned int *u = reinterpret_cast<unsigned int *>(slot);
-    const unsigned int bits = bf16_mag << 16;
-    if (__hip_atomic_load(u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= bits) return;
-    atomicMax(u, bits);
+    if (__hip_atomic_load(u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= f32_mag) return;
+    atomicMax(u, f32_mag);
+}
+__device__ __forceinline__ void fold_amax(float *slot, uint32_t bf16_mag) { fold_amax_bits(slot, bf16_mag << 16); }
+
+// Four float32 values already multiplied by the scale -> one dword of four codes.  The clamp +
+// hardware conversion is exact for everything but NaN, which takes the exact encoder.
+template <int FMT>
+__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) {
+    if (a == a && b == b && c == c && d == d)
+        return pack4<FMT>(clamp_fmt<FMT>(a), clamp_fmt<FMT>(b), clamp_fmt<FMT>(c), clamp_fmt<FMT>(d));
+    return encode_exact<FMT>(a) | (encode_exact<FMT>(b) << 8) | (encode_exact<FMT>(c) << 16) |
+           (encode_exact<FMT>(d) << 24);
 }
 
 }  // namespace fp8ds

@@ -71,15 +71,33 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
 }
 }  // namespace
 
+// acc * a_scale_inv * b_scale_inv + bias: one product, then one fused multiply-add.  Every
+// epilogue uses exactly this sequence, so all output dtypes see the same float32 value.
+__device__ __forceinline__ float dequant_bias(float acc, float sa, float sb, float b) {
+    return __builtin_fmaf(acc * sa, sb, b);
+}
+
+// FP8 output (OUT 2 = E4M3, 3 = E5M2): D is encoded with its own scale, max |D| (float32, before
+// the scale) is folded into an amax slot, and block 0 records 1/scale as the output's private
+// inverse scale.  Ignored for bfloat16 / float32 output.
+struct OutQuant {
+    const float *scale;
+    float *scale_inv_out;
+    float *amax;
+};
+
 // Epilogue of one wave's 128 x 128 sub-tile at (row0, col0).  Accumulator element e of lane l in
 // a 32 x 32 MFMA tile is row (e / 4) * 8 + (l / 32) * 4 + e % 4, column l % 32.
 template <int OUT>
 __device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], const float *__restrict__ a_sinv,
                                          const float *__restrict__ b_sinv, const uint16_t *__restrict__ bias,
                                          void *__restrict__ D, int64_t ldd, int M, int N, int row0, int col0,
-                                         int lane) {
+                                         int lane, OutQuant oq) {
     const int frow = lane & 31, fhalf = lane >> 5;
     const float sa = *a_sinv, sb = *b_sinv;
+    float ds = 0.f;
+    if constexpr (OUT >= 2) ds = *oq.scale;
+    uint32_t amag = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int col = col0 + j * 32 + frow;
@@ -91,14 +109,23 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], const float 
             for (int e = 0; e < 16; ++e) {
                 const int row = row0 + i * 32 + (e >> 2) * 8 + fhalf * 4 + (e & 3);
                 if (row < M) {
-                    const float v = acc[i][j][e] * sa * sb + bv;
-                    if constexpr (OUT == 0)
+                    const float v = dequant_bias(acc[i][j][e], sa, sb, bv);
+                    if constexpr (OUT == 0) {
                         reinterpret_cast<uint16_t *>(D)[(int64_t)row * ldd + col] = f32_to_bf16_rne(v);
-                    else
+                    } else if constexpr (OUT == 1) {
                         reinterpret_cast<float *>(D)[(int64_t)row * ldd + col] = v;
+                    } else {
+                        amag = max(amag, __float_as_uint(v) & 0x7FFFFFFFu);
+                        reinterpret_cast<uint8_t *>(D)[(int64_t)row * ldd + col] =
+                            (uint8_t)encode_exact<OUT - 2>(v * ds);
+                    }
                 }
             }
         }
+    }
+    if constexpr (OUT >= 2) {
+        amag = wave_max_u32(amag);
+        if (lane == 0) fold_amax_bits(oq.amax, amag);
     }
 }
 
@@ -114,18 +141,23 @@ template <int OUT>
 __device__ __forceinline__ void epilogue_staged(const f32x16 (&acc)[4][4], const float *__restrict__ a_sinv,
                                                 const float *__restrict__ b_sinv, const uint16_t *__restrict__ bias,
                                                 void *__restrict__ D, int64_t ldd, int M, int N, int row0, int col0,
-                                                int lane, uint8_t *wlds) {
+                                                int lane, uint8_t *wlds, OutQuant oq) {
     const int frow = lane & 31, fhalf = lane >> 5;
     const float sa = *a_sinv, sb = *b_sinv;
-    const bool vec_ok = ((reinterpret_cast<uintptr_t>(D) & 15u) == 0) && (ldd % (OUT == 0 ? 8 : 4) == 0);
-    // bias of the 16 columns this lane holds in column block j
+    constexpr int kElemsPer16 = OUT == 0 ? 8 : OUT == 1 ? 4 : 16;
+    const bool vec_ok = ((reinterpret_cast<uintptr_t>(D) & 15u) == 0) && (ldd % kElemsPer16 == 0);
+    // bias of the 16 columns this lane holds in column block j.  Columns past N read bias[N - 1]:
+    // their operand rows are clamped to row N - 1 of B, so every value a lane holds outside the
+    // output (rows past M read row M - 1 of A) is bit-identical to an element inside it.  Such
+    // values are never stored, and the FP8 output's amax can take the max over the whole
+    // sub-tile without masking.
     auto load_bias = [&](int j, float (&bv)[4][4]) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int col = col0 + j * 32 + q * 8 + fhalf * 4 + u;
-                bv[q][u] = (bias != nullptr && col < N) ? __uint_as_float((uint32_t)bias[col] << 16) : 0.f;
+                const int col = min(col0 + j * 32 + q * 8 + fhalf * 4 + u, N - 1);
+                bv[q][u] = bias != nullptr ? __uint_as_float((uint32_t)bias[col] << 16) : 0.f;
             }
     };
     if constexpr (OUT == 0) {
@@ -140,7 +172,7 @@ __device__ __forceinline__ void epilogue_staged(const f32x16 (&acc)[4][4], const
                     const int r = i * 32 + frow, sl = j * 8 + q * 2 + fhalf;
                     float v[4];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) v[u] = acc[i][j][q * 4 + u] * sa * sb + bv[q][u];
+                    for (int u = 0; u < 4; ++u) v[u] = dequant_bias(acc[i][j][q * 4 + u], sa, sb, bv[q][u]);
                     const u32x2 pk = {(uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16),
                                       (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16)};
                     *reinterpret_cast<u32x2 *>(wlds + r * 256 + ((sl ^ (r & 31)) << 3)) = pk;
@@ -169,7 +201,7 @@ __device__ __forceinline__ void epilogue_staged(const f32x16 (&acc)[4][4], const
                 }
             }
         }
-    } else {
+    } else if constexpr (OUT == 1) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -183,10 +215,10 @@ __device__ __forceinline__ void epilogue_staged(const f32x16 (&acc)[4][4], const
                         const int i = h * 2 + ii;
                         const int r = ii * 32 + frow, sl = j * 8 + q * 2 + fhalf;
                         u32x4 pk;
-                        pk.x = __float_as_uint(acc[i][j][q * 4 + 0] * sa * sb + bv[q][0]);
-                        pk.y = __float_as_uint(acc[i][j][q * 4 + 1] * sa * sb + bv[q][1]);
-                        pk.z = __float_as_uint(acc[i][j][q * 4 + 2] * sa * sb + bv[q][2]);
-                        pk.w = __float_as_uint(acc[i][j][q * 4 + 3] * sa * sb + bv[q][3]);
+                        pk.x = __float_as_uint(dequant_bias(acc[i][j][q * 4 + 0], sa, sb, bv[q][0]));
+                        pk.y = __float_as_uint(dequant_bias(acc[i][j][q * 4 + 1], sa, sb, bv[q][1]));
+                        pk.z = __float_as_uint(dequant_bias(acc[i][j][q * 4 + 2], sa, sb, bv[q][2]));
+                        pk.w = __float_as_uint(dequant_bias(acc[i][j][q * 4 + 3], sa, sb, bv[q][3]));
                         *reinterpret_cast<u32x4 *>(wlds + r * 512 + ((sl ^ (r & 31)) << 4)) = pk;
                     }
             }
@@ -213,6 +245,57 @@ __device__ __forceinline__ void epilogue_staged(const f32x16 (&acc)[4][4], const
             __builtin_amdgcn_s_waitcnt(0xC07F);
             __builtin_amdgcn_wave_barrier();
         }
+    } else {
+        // FP8: 128 rows x 128 bytes = 16 KB; row r at r * 128, 4-byte slot s (columns 4 s ..
+        // 4 s + 3) stored at slot s ^ (r & 31).
+        constexpr int F = OUT - 2;
+        const float ds = *oq.scale;
+        uint32_t amag = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float bv[4][4];
+            load_bias(j, bv);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = i * 32 + frow, sl = j * 8 + q * 2 + fhalf;
+                    float v[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        v[u] = dequant_bias(acc[i][j][q * 4 + u], sa, sb, bv[q][u]);
+                        amag = max(amag, __float_as_uint(v[u]) & 0x7FFFFFFFu);
+                    }
+                    const uint32_t w = encode4<F>(v[0] * ds, v[1] * ds, v[2] * ds, v[3] * ds);
+                    *reinterpret_cast<uint32_t *>(wlds + r * 128 + ((sl ^ (r & 31)) << 2)) = w;
+                }
+        }
+        amag = wave_max_u32(amag);
+        if (lane == 0) fold_amax_bits(oq.amax, amag);
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
+        // 16-byte chunk ch of row r = slots 4 ch .. 4 ch + 3, stored in the aligned group
+        // (4 ch) ^ (x & ~3), x = r & 31, with slot 4 ch + k at position k ^ (x & 3).
+#pragma unroll
+        for (int pq = 0; pq < 16; ++pq) {
+            const int r = pq * 8 + (lane >> 3), ch = lane & 7;
+            const int x = r & 31;
+            u32x4 v = *reinterpret_cast<const u32x4 *>(wlds + r * 128 + (((4 * ch) ^ (x & ~3)) << 2));
+            if (x & 1) v = v.yxwz;
+            if (x & 2) v = v.zwxy;
+            const int row = row0 + r, col = col0 + ch * 16;
+            if (row < M && col < N) {
+                uint8_t *dst = reinterpret_cast<uint8_t *>(D) + (int64_t)row * ldd + col;
+                if (vec_ok && col + 15 < N) {
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst));
+                } else {
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int u = 0; u < 16; ++u)
+                        if (col + u < N) dst[u] = (uint8_t)(w[u >> 2] >> (8 * (u & 3)));
+                }
+            }
+        }
     }
 }
 
@@ -223,7 +306,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias(const uint8_t *__rest
                                                            const float *__restrict__ b_sinv,
                                                            const uint16_t *__restrict__ bias,
                                                            void *__restrict__ D, int64_t ldd, int M, int N,
-                                                           int K, int tiles_m, int tiles_n) {
+                                                           int K, int tiles_m, int tiles_n, OutQuant oq) {
+    if constexpr (OUT >= 2)
+        if (blockIdx.x == 0 && threadIdx.x == 0 && oq.scale_inv_out != nullptr) *oq.scale_inv_out = 1.0f / *oq.scale;
     __shared__ __align__(16) uint8_t smem[kLdsBytes];
 
     int tm, tn;
@@ -329,7 +414,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias(const uint8_t *__rest
         __syncthreads();
     }
 
-    epilogue<OUT>(acc, a_sinv, b_sinv, bias, D, ldd, M, N, m0 + wm * 128, n0 + wn * 128, lane);
+    epilogue<OUT>(acc, a_sinv, b_sinv, bias, D, ldd, M, N, m0 + wm * 128, n0 + wn * 128, lane, oq);
 }
 
 
@@ -361,7 +446,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias_pipe(const uint8_t *_
                                                                 const float *__restrict__ b_sinv,
                                                                 const uint16_t *__restrict__ bias,
                                                                 void *__restrict__ D, int64_t ldd, int M, int N,
-                                                                int K, int tiles_m, int tiles_n) {
+                                                                int K, int tiles_m, int tiles_n, OutQuant oq) {
+    if constexpr (OUT >= 2)
+        if (blockIdx.x == 0 && threadIdx.x == 0 && oq.scale_inv_out != nullptr) *oq.scale_inv_out = 1.0f / *oq.scale;
     __shared__ __align__(16) uint8_t st0[kPStage];
     __shared__ __align__(16) uint8_t st1[kPStage];
     __shared__ __align__(16) uint8_t st2[kPStage];
@@ -489,32 +576,58 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias_pipe(const uint8_t *_
 #undef FP8DS_STEP
     __syncthreads();   // every wave is done reading the operand stages
     uint8_t *wl = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
-    epilogue_staged<OUT>(acc, a_sinv, b_sinv, bias, D, ldd, M, N, m0 + wm * 128, n0 + wn * 128, lane, wl);
+    epilogue_staged<OUT>(acc, a_sinv, b_sinv, bias, D, ldd, M, N, m0 + wm * 128, n0 + wn * 128, lane, wl, oq);
 }
 
 // D = bias broadcast (K == 0): no products at all.
 template <int OUT>
 __global__ __launch_bounds__(256) void k_bias_only(const uint16_t *__restrict__ bias, void *__restrict__ D,
-                                                   int64_t ldd, int M, int N) {
+                                                   int64_t ldd, int M, int N, OutQuant oq) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (int64_t)M * N) return;
-    const int64_t m = idx / N, n = idx % N;
-    const float v = bias != nullptr ? __uint_as_float((uint32_t)bias[n] << 16) : 0.f;
-    if constexpr (OUT == 0)
-        reinterpret_cast<uint16_t *>(D)[m * ldd + n] = f32_to_bf16_rne(v);
-    else
-        reinterpret_cast<float *>(D)[m * ldd + n] = v;
+    uint32_t amag = 0;
+    if (idx < (int64_t)M * N) {
+        const int64_t m = idx / N, n = idx % N;
+        // 0 + bias, as for K > 0 with a zero sum (a -0 bias gives +0)
+        const float v = (bias != nullptr ? __uint_as_float((uint32_t)bias[n] << 16) : 0.f) + 0.0f;
+        if constexpr (OUT == 0) {
+            reinterpret_cast<uint16_t *>(D)[m * ldd + n] = f32_to_bf16_rne(v);
+        } else if constexpr (OUT == 1) {
+            reinterpret_cast<float *>(D)[m * ldd + n] = v;
+        } else {
+            amag = __float_as_uint(v) & 0x7FFFFFFFu;
+            reinterpret_cast<uint8_t *>(D)[m * ldd + n] = (uint8_t)encode_exact<OUT - 2>(v * *oq.scale);
+        }
+    }
+    if constexpr (OUT >= 2) {
+        if (blockIdx.x == 0 && threadIdx.x == 0 && oq.scale_inv_out != nullptr) *oq.scale_inv_out = 1.0f / *oq.scale;
+        amag = wave_max_u32(amag);
+        if ((threadIdx.x & 63) == 0) fold_amax_bits(oq.amax, amag);
+    }
 }
 
 hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64_t lda, const uint8_t *B, int fb,
                             const float *b_sinv, int64_t ldb, const uint16_t *bias, void *D, int64_t ldd,
-                            int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t st) {
-    if (M == 0 || N == 0) return hipSuccess;
+                            int out_dtype, int64_t M, int64_t N, int64_t K, const float *d_scale,
+                            float *d_sinv_out, float *d_amax, hipStream_t st) {
+    const OutQuant oq{d_scale, d_sinv_out, d_amax};
+    if (M == 0 || N == 0) {
+        // nothing to write but the output's inverse scale
+        if (out_dtype >= 2 && d_sinv_out != nullptr) {
+            if (out_dtype == 2) k_bias_only<2><<<1, 64, 0, st>>>(bias, D, ldd, 0, 0, oq);
+            else k_bias_only<3><<<1, 64, 0, st>>>(bias, D, ldd, 0, 0, oq);
+            return hipGetLastError();
+        }
+        return hipSuccess;
+    }
     if (K == 0) {
         const int64_t total = M * N;
         dim3 grid((unsigned)((total + 255) / 256));
-        if (out_dtype == 0) k_bias_only<0><<<grid, 256, 0, st>>>(bias, D, ldd, (int)M, (int)N);
-        else k_bias_only<1><<<grid, 256, 0, st>>>(bias, D, ldd, (int)M, (int)N);
+        switch (out_dtype) {
+            case 0: k_bias_only<0><<<grid, 256, 0, st>>>(bias, D, ldd, (int)M, (int)N, oq); break;
+            case 1: k_bias_only<1><<<grid, 256, 0, st>>>(bias, D, ldd, (int)M, (int)N, oq); break;
+            case 2: k_bias_only<2><<<grid, 256, 0, st>>>(bias, D, ldd, (int)M, (int)N, oq); break;
+            default: k_bias_only<3><<<grid, 256, 0, st>>>(bias, D, ldd, (int)M, (int)N, oq); break;
+        }
         return hipGetLastError();
     }
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
@@ -524,22 +637,25 @@ hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64
     do {                                                                                                   \
         if (pipe)                                                                                          \
             k_gemm_bias_pipe<FA_, FB_, O_><<<grid, dim3(kThreads), 0, st>>>(                               \
-                A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, tiles_m, tiles_n);   \
+                A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, tiles_m, tiles_n, oq); \
         else                                                                                               \
             k_gemm_bias<FA_, FB_, O_><<<grid, dim3(kThreads), 0, st>>>(                                    \
-                A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, tiles_m, tiles_n);   \
+                A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, tiles_m, tiles_n, oq); \
     } while (0)
-    const int sel = fa * 4 + fb * 2 + out_dtype;
-    switch (sel) {
-        case 0: FP8DS_GEMM(kE4M3, kE4M3, 0); break;
-        case 1: FP8DS_GEMM(kE4M3, kE4M3, 1); break;
-        case 2: FP8DS_GEMM(kE4M3, kE5M2, 0); break;
-        case 3: FP8DS_GEMM(kE4M3, kE5M2, 1); break;
-        case 4: FP8DS_GEMM(kE5M2, kE4M3, 0); break;
-        case 5: FP8DS_GEMM(kE5M2, kE4M3, 1); break;
-        case 6: FP8DS_GEMM(kE5M2, kE5M2, 0); break;
-        default: FP8DS_GEMM(kE5M2, kE5M2, 1); break;
+#define FP8DS_GEMM_OUT(FA_, FB_)                                                                           \
+    switch (out_dtype) {                                                                                   \
+        case 0: FP8DS_GEMM(FA_, FB_, 0); break;                                                            \
+        case 1: FP8DS_GEMM(FA_, FB_, 1); break;                                                            \
+        case 2: FP8DS_GEMM(FA_, FB_, 2); break;                                                            \
+        default: FP8DS_GEMM(FA_, FB_, 3); break;                                                           \
     }
+    switch (fa * 2 + fb) {
+        case 0: FP8DS_GEMM_OUT(kE4M3, kE4M3) break;
+        case 1: FP8DS_GEMM_OUT(kE4M3, kE5M2) break;
+        case 2: FP8DS_GEMM_OUT(kE5M2, kE4M3) break;
+        default: FP8DS_GEMM_OUT(kE5M2, kE5M2) break;
+    }
+#undef FP8DS_GEMM_OUT
 #undef FP8DS_GEMM
     return hipGetLastError();
 }

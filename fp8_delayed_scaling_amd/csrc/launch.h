@@ -17,12 +17,17 @@ hipError_t launch_dbias_cast_transpose(const uint16_t *dy, int64_t rows, int64_t
                                        int fmt, uint8_t *out, uint8_t *out_t, float *sinv_out,
                                        float *amax_slot, float *dbias, void *ws, hipStream_t st);
 
+hipError_t launch_fp8_transpose(const uint8_t *in, int64_t rows, int64_t cols, uint8_t *out_t, const float *noop,
+                                hipStream_t st);
+
 constexpr int kMaxScaleTensors = 4096;
 hipError_t launch_scale_update(float *hist, int64_t L, int64_t T, float *scale, float *scale_inv,
                                const int32_t *fmts_host, int32_t margin, hipStream_t st);
 
+// out_dtype: 0 bfloat16, 1 float32, 2 E4M3, 3 E5M2 (the last two use d_scale, d_sinv_out, d_amax).
 hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64_t lda, const uint8_t *B, int fb,
                             const float *b_sinv, int64_t ldb, const uint16_t *bias, void *D, int64_t ldd,
-                            int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t st);
+                            int out_dtype, int64_t M, int64_t N, int64_t K, const float *d_scale,
+                            float *d_sinv_out, float *d_amax, hipStream_t st);
 
 }  // namespace fp8ds

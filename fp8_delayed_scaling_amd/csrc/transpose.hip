@@ -1,0 +1,92 @@
+// transpose.hip -- FP8 -> FP8 transpose of a tensor that already exists: the lazy fill of a
+// Float8Tensor's transpose cache ("[PyTorch] Refactor FP8 workspaces in linear modules",
+// "grown in scope" first bullet: transpose_2d(cache=True) and lazy transpose caching;
+// "[PyTorch] cuda graph support", transpose-cache thread: the transpose of an FP8 dy that
+// carries no cache, and the noop flag in transpose that keeps a cached weight transpose across
+// microbatches).  Codes are moved, never re-encoded.
+//
+// HBM-bound: 1 byte read + 1 byte written per element.  A block of 256 threads owns a 256 x 256
+// byte tile and each thread one 16 x 16 byte block: 16 loads of 16 bytes (one row segment
+// each), a register transpose made of sixteen 4 x 4 byte transposes, and 16 stores of 16 bytes
+// (one segment of each of 16 output rows).  Lane l of wave w takes row block (w / 2) * 8 + l % 8
+// and column block (w % 2) * 8 + l / 8, so one load instruction of a wave reads 8 rows x 128
+// contiguous bytes and one store instruction writes 8 output rows x 128 contiguous bytes.  No
+// LDS.  The vector path needs rows and cols multiples of 16 and 16-byte aligned buffers;
+// otherwise each thread moves its block byte by byte with bounds checks.
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8ds {
+
+namespace {
+constexpr int kTT = 256;   // tile edge (bytes)
+
+// 4 x 4 byte transpose: byte k of a, b, c, d is element (row 0..3, column k); o_k receives
+// column k in row order.  Two rounds of two-source byte merges (the compiler emits v_perm_b32).
+__device__ __forceinline__ void tr4(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t &o0, uint32_t &o1,
+                                    uint32_t &o2, uint32_t &o3) {
+    const uint32_t ab_lo = (a & 0xFFu) | ((b & 0xFFu) << 8) | ((a & 0xFF00u) << 8) | ((b & 0xFF00u) << 16);
+    const uint32_t ab_hi = ((a & 0xFF0000u) >> 16) | ((b & 0xFF0000u) >> 8) | ((a & 0xFF000000u) >> 8) |
+                           (b & 0xFF000000u);
+    const uint32_t cd_lo = (c & 0xFFu) | ((d & 0xFFu) << 8) | ((c & 0xFF00u) << 8) | ((d & 0xFF00u) << 16);
+    const uint32_t cd_hi = ((c & 0xFF0000u) >> 16) | ((d & 0xFF0000u) >> 8) | ((c & 0xFF000000u) >> 8) |
+                           (d & 0xFF000000u);
+    o0 = (ab_lo & 0xFFFFu) | (cd_lo << 16);
+    o1 = (ab_lo >> 16) | (cd_lo & 0xFFFF0000u);
+    o2 = (ab_hi & 0xFFFFu) | (cd_hi << 16);
+    o3 = (ab_hi >> 16) | (cd_hi & 0xFFFF0000u);
+}
+}  // namespace
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void k_fp8_transpose(const uint8_t *__restrict__ in, int64_t rows, int64_t cols,
+                                                       uint8_t *__restrict__ out_t, const float *__restrict__ noop,
+                                                       int64_t tiles_c) {
+    if (noop != nullptr && *noop == 1.0f) return;
+    const int64_t tile = blockIdx.x;
+    const int64_t r0 = (tile / tiles_c) * kTT, c0 = (tile % tiles_c) * kTT;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t rb = r0 + (int64_t)((wave >> 1) * 8 + (lane & 7)) * 16;
+    const int64_t cb = c0 + (int64_t)((wave & 1) * 8 + (lane >> 3)) * 16;
+    if (rb >= rows || cb >= cols) return;
+    if constexpr (VEC) {
+        // rows and cols are multiples of 16, so the whole 16 x 16 block is in range
+        uint32_t R[16][4];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(in + (rb + j) * cols + cb));
+            R[j][0] = v.x; R[j][1] = v.y; R[j][2] = v.z; R[j][3] = v.w;
+        }
+        uint32_t O[16][4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                tr4(R[4 * d][w], R[4 * d + 1][w], R[4 * d + 2][w], R[4 * d + 3][w], O[4 * w][d], O[4 * w + 1][d],
+                    O[4 * w + 2][d], O[4 * w + 3][d]);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const u32x4 v = {O[c][0], O[c][1], O[c][2], O[c][3]};
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(out_t + (cb + c) * rows + rb));
+        }
+    } else {
+        for (int j = 0; j < 16 && rb + j < rows; ++j)
+            for (int c = 0; c < 16 && cb + c < cols; ++c) out_t[(cb + c) * rows + rb + j] = in[(rb + j) * cols + cb + c];
+    }
+}
+
+hipError_t launch_fp8_transpose(const uint8_t *in, int64_t rows, int64_t cols, uint8_t *out_t, const float *noop,
+                                hipStream_t st) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    const int64_t tr = (rows + kTT - 1) / kTT, tc = (cols + kTT - 1) / kTT;
+    const bool vec = rows % 16 == 0 && cols % 16 == 0 && (reinterpret_cast<uintptr_t>(in) & 15u) == 0 &&
+                     (reinterpret_cast<uintptr_t>(out_t) & 15u) == 0;
+    const dim3 grid((unsigned)(tr * tc));
+    if (vec)
+        k_fp8_transpose<true><<<grid, dim3(256), 0, st>>>(in, rows, cols, out_t, noop, tc);
+    else
+        k_fp8_transpose<false><<<grid, dim3(256), 0, st>>>(in, rows, cols, out_t, noop, tc);
+    return hipGetLastError();
+}
+
+}  // namespace fp8ds

@@ -18,7 +18,7 @@
  *     "grown in scope", first bullet; [CG] feature list, persistent transposes).
  *   - bfloat16 tensors are passed as uint16_t bit patterns, FP8 tensors as uint8_t codes.
  *     2-D tensors are row-major and densely packed unless a leading dimension is given.
- *   - Device pointers must be 16-byte aligned.
+ *   - Device pointers must be 16-byte aligned unless a call's comment says otherwise.
  *   - Scales live on the device (float32 scalars), so no call reads them on the host.
  *   - Return value: FP8DS_OK (0) or a negative fp8ds_status.  Arguments are checked on the
  *     host before anything is launched; a rejected call launches nothing.  After launching,
@@ -184,6 +184,46 @@ int fp8_gemm_bias_chunked(const uint8_t *A, int fa, const float *a_scale_inv, in
                           const uint16_t *bias, void *D, int64_t ldd, int out_dtype,
                           int64_t M, int64_t N, int64_t K, int n_chunks,
                           const hipStream_t *chunk_streams, hipStream_t stream);
+
+/*
+ * fp8_gemm_bias_fp8 -- fp8_gemm_bias whose output is itself an FP8 tensor with its own scale
+ * ([CG] transpose-cache thread: FP8Linear.backward passes out=dx._data, so the GEMM writes
+ * straight into the data of a Float8Tensor).
+ *
+ *   v[m, n] = (sum_k A[m, k] * B[n, k]) * (*a_scale_inv) * (*b_scale_inv) + bias[n]   (float32)
+ *   D[m, n] = saturating round-to-nearest-even code (format d_fmt) of v[m, n] * (*d_scale)
+ *   *d_amax_slot = max(*d_amax_slot, max |v|)          (amax of the output before its scale)
+ *   *d_scale_inv_out = 1.0f / (*d_scale)               (the output's private inverse scale)
+ *
+ * A, B, bias, M, N, K and their requirements are those of fp8_gemm_bias.  D: [M, N] codes with
+ * row stride ldd >= N bytes, any alignment (16-byte aligned D with ldd % 16 == 0 takes the
+ * vector stores).  d_scale is required; d_scale_inv_out and d_amax_slot may be NULL (not
+ * written).  The amax fold is an atomic max, so d_amax_slot may be an amax-history slot that
+ * other kernels also fold into.  NaN values give code 0x7F and a NaN amax, as in the casts.
+ * With M or N == 0 only *d_scale_inv_out is written.
+ */
+int fp8_gemm_bias_fp8(const uint8_t *A, int fa, const float *a_scale_inv, int64_t lda,
+                      const uint8_t *B, int fb, const float *b_scale_inv, int64_t ldb,
+                      const uint16_t *bias, uint8_t *D, int64_t ldd, int d_fmt,
+                      const float *d_scale, float *d_scale_inv_out, float *d_amax_slot,
+                      int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * fp8_transpose -- transpose cache of an FP8 tensor that already exists ([WS] "grown in scope",
+ * first bullet: transpose_2d(cache=True) and lazy transpose caching; [CG] transpose-cache
+ * thread: dy.transpose() of an FP8 dy without a cache, and the noop flag in transpose used for
+ * weight caching across microbatches).
+ *
+ *   out_t[j, i] = in[i, j]     in: [rows, cols] codes, out_t: [cols, rows] codes
+ *
+ * The codes are copied, not re-encoded (the tensor's scale and scale_inv are unchanged).
+ * noop: NULL, or a device float; when *noop == 1.0f at run time the kernel writes nothing and
+ * the cache keeps its previous contents.  Any alignment is accepted (16-byte aligned buffers
+ * with rows and cols multiples of 16 take the vector path).  rows or cols == 0 launches
+ * nothing.  in and out_t must not overlap.
+ */
+int fp8_transpose(const uint8_t *in, int64_t rows, int64_t cols, uint8_t *out_t, const float *noop,
+                  hipStream_t stream);
 
 /*
  * fp8_linear_fwd -- forward of the FP8 linear layer y = x W^T + bias ([WS] description: one

@@ -85,6 +85,13 @@ def uniform(seed: int, start: int, count: int) -> np.ndarray:
     return (w >> np.uint64(11)).astype(np.float64) * (1.0 / 9007199254740992.0)
 
 
+def random_bytes(seed: int, shape) -> np.ndarray:
+    """Uniform random bytes of ``shape``: the little-endian bytes of stream ``seed``'s words."""
+    n = int(np.prod(shape))
+    w = splitmix64(seed, 0, (n + 7) // 8)
+    return np.ascontiguousarray(w.astype("<u8").view(np.uint8)[:n]).reshape(shape)
+
+
 def normal_f64(seed: int, n: int, std: float) -> np.ndarray:
     """``n`` float64 samples of N(0, std^2) by Box-Muller, drawn chunk by chunk."""
     out = np.empty(n, dtype=np.float64)

@@ -20,8 +20,8 @@ def _declared():
 def test_header_declares_the_hot_path():
     names = _declared()
     for n in ("fp8_cast_amax", "fp8_cast_transpose", "fp8_dbias_cast_transpose", "fp8_dbias_workspace_bytes",
-              "fp8_scale_update", "fp8_gemm_bias", "fp8_gemm_bias_chunked", "fp8_linear_fwd", "fp8_linear_bwd",
-              "fp8ds_status_string", "fp8ds_version"):
+              "fp8_scale_update", "fp8_gemm_bias", "fp8_gemm_bias_chunked", "fp8_gemm_bias_fp8", "fp8_transpose",
+              "fp8_linear_fwd", "fp8_linear_bwd", "fp8ds_status_string", "fp8ds_version"):
         assert n in names, n
 
 
@@ -112,3 +112,46 @@ def test_linear_validation():
     # backward needs M and N multiples of 16
     assert L.fp8_linear_bwd(A16, 24, 16, 16, A16, None, A16, A16, A16, None, None, 0, A16, A16, A16, A16, A16,
                             A16, 0, None) == -2
+
+
+def test_gemm_fp8_out_validation():
+    L = F.lib()
+    g = L.fp8_gemm_bias_fp8
+    ok = dict(A=A16, fa=0, sa=A16, lda=64, B=A16, fb=0, sb=A16, ldb=64, bias=None, D=A16, ldd=32, d_fmt=0,
+              ds=A16, dsinv=None, damax=None, M=16, N=32, K=64)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return g(a["A"], a["fa"], a["sa"], a["lda"], a["B"], a["fb"], a["sb"], a["ldb"], a["bias"], a["D"], a["ldd"],
+                 a["d_fmt"], a["ds"], a["dsinv"], a["damax"], a["M"], a["N"], a["K"], None)
+
+    assert call(d_fmt=2) == -4                 # unknown output format
+    assert call(fa=3) == -4
+    assert call(ds=None) == -1                 # the output scale is required
+    assert call(ds=A16 + 2) == -3
+    assert call(damax=A16 + 1) == -3
+    assert call(D=None) == -1
+    assert call(K=40) == -2                    # K % 16
+    assert call(ldd=31) == -2                  # ldd < N
+    assert call(lda=48) == -2                  # lda < K
+    assert call(A=A16 + 8) == -3
+    assert call(M=0) == 0                      # empty output, no inverse scale asked: nothing launched
+
+
+def test_fp8_out_dtype_codes_stay_private():
+    """The plain GEMM accepts only the two public output dtypes."""
+    L = F.lib()
+    args = [A16, 0, A16, 64, A16, 0, A16, 64, None, A16, 32]
+    assert L.fp8_gemm_bias(*args, 2, 16, 32, 64, None) == -4
+    assert L.fp8_gemm_bias(*args, 3, 16, 32, 64, None) == -4
+    assert L.fp8_gemm_bias_chunked(*args, 2, 16, 32, 64, 2, None, None) == -4
+
+
+def test_transpose_validation():
+    L = F.lib()
+    assert L.fp8_transpose(None, 4, 4, A16, None, None) == -1
+    assert L.fp8_transpose(A16, 4, 4, None, None, None) == -1
+    assert L.fp8_transpose(A16, -1, 4, A16, None, None) == -2
+    assert L.fp8_transpose(A16, 4, 4, A16, A16 + 2, None) == -3      # misaligned noop flag
+    assert L.fp8_transpose(None, 0, 4, None, None, None) == 0         # empty: nothing
+    assert L.fp8_transpose(A16, 1, 1 << 40, A16, None, None) == -2    # too many tiles

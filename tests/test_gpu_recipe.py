@@ -300,3 +300,87 @@ def test_resume_from_copied_state():
     torch.cuda.synchronize()
     for name in ("hist", "scale", "scale_inv", "sinv", "y", "dx", "dw"):
         assert torch.equal(getattr(a, name).view(torch.uint8), getattr(c, name).view(torch.uint8)), name
+
+
+def test_weight_caching_across_microbatches_in_a_graph():
+    """One microbatch (fwd with the weight's noop flag, lazy transpose of x, bwd) captured once
+    and replayed for 3 microbatches x 3 steps, the scale update captured in a second graph run
+    at each step's end.  The host sets the device flag to 0 on a step's first microbatch (recast
+    W and refresh its transpose cache) and to 1 on the others (reuse the cached FP8 weight, its
+    transpose and its private inverse scale), and writes new x / dy (and, between steps, a new W)
+    into the captured input buffers.  Every replay is checked against the oracle run through the
+    same sequence: FP8 tensors, inverse scales, history and scales bit-exact, y / dx / dW within
+    the GEMM tolerance.  W is also changed in place inside a step, which a cached microbatch must
+    not see."""
+    M, N, K = 256, 384, 512
+    lay = Layer(M, N, K)
+    x = torch.empty((M, K), device=DEV, dtype=torch.bfloat16)
+    w = torch.empty((N, K), device=DEV, dtype=torch.bfloat16)
+    b = bf16_dev(S.normal_bf16(S.seed_for(5, 2), (N,), 0.1))
+    dy = torch.empty((M, N), device=DEV, dtype=torch.bfloat16)
+    bh = S.normal_bf16(S.seed_for(5, 2), (N,), 0.1)
+    cap = torch.cuda.Stream()
+    g_mb, g_up = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g_mb, stream=cap):
+        # forward: x cast without its transpose (x8_t = NULL), W cast+transpose under the flag
+        F.fp8_linear_fwd(x, w, b, lay.scale[0:1], lay.hist[0, 0:1], lay.x8, None, lay.sinv[0:1],
+                         lay.scale[1:2], lay.hist[0, 1:2], lay.w8, lay.w8t, lay.sinv[1:2], lay.noop, lay.y,
+                         stream=cap)
+        # backward needs x^T: the lazy transpose of the FP8 x fills the cache
+        F.fp8_transpose(lay.x8, lay.x8t, stream=cap)
+        lay.bwd(dy, stream=cap)
+    with torch.cuda.graph(g_up, stream=cap):
+        lay.update(stream=cap)
+    for t in (lay.hist, lay.sinv):
+        t.zero_()
+    lay.scale.fill_(1.0)
+    lay.scale_inv.fill_(1.0)
+    torch.cuda.synchronize()
+
+    h = np.zeros((16, 3), np.float32)
+    s = np.ones(3, np.float32)
+    si = np.ones(3, np.float32)
+    cached = None            # oracle's cached FP8 weight: (w8, w8t, w_sinv)
+    for step in range(3):
+        wh = S.normal_bf16(S.seed_for(5, 16 + step), (N, K), 0.05)
+        w.copy_(bf16_dev(wh))
+        for mb in range(3):
+            print(f"weight caching step {step} microbatch {mb}", flush=True)
+            xh = S.normal_bf16(S.seed_for(6, 4 * step + mb), (M, K), 1.0)
+            dyh = S.normal_bf16(S.seed_for(7, 4 * step + mb), (M, N), 0.01)
+            x.copy_(bf16_dev(xh))
+            dy.copy_(bf16_dev(dyh))
+            if mb == 2:
+                w.mul_(-3.0)      # an in-place change a cached microbatch must not see
+            first = mb == 0
+            lay.noop.fill_(0.0 if first else 1.0)
+            g_mb.replay()
+            torch.cuda.synchronize()
+            # oracle, same sequence
+            x8, x_amax, x_sinv = oracle.cast_amax(xh, s[0], F.E4M3, h[0, 0])
+            if first:
+                w8, w8t, w_amax, w_sinv = oracle.cast_transpose(wh, s[1], F.E4M3, h[0, 1])
+                cached = (w8, w8t, w_sinv)
+                h[0, 1] = w_amax
+            w8, w8t, w_sinv = cached
+            h[0, 0] = x_amax
+            x8t = oracle.fp8_transpose(x8)
+            y = oracle.gemm_bias(x8, F.E4M3, x_sinv, w8, F.E4M3, w_sinv, bh)
+            bw = oracle.linear_bwd(dyh, s[2], x8t, x_sinv, w8t, w_sinv)
+            # the dy amax folds into the slot across microbatches
+            _, _, dy_amax, _ = oracle.cast_transpose(dyh, s[2], F.E5M2, h[0, 2])
+            h[0, 2] = dy_amax
+            assert np.array_equal(u8_host(lay.x8), x8) and np.array_equal(u8_host(lay.x8t), x8t)
+            assert np.array_equal(u8_host(lay.w8), w8) and np.array_equal(u8_host(lay.w8t), w8t)
+            assert np.array_equal(u8_host(lay.dy8t), bw["dy8t"])
+            assert _same(lay.sinv.cpu().numpy(), [x_sinv, w_sinv, bw["dy_sinv"]])
+            assert _same(lay.hist.cpu().numpy(), h), (step, mb)
+            gemm_close(to_f64(lay.y), y, bf16_out=True)
+            gemm_close(to_f64(lay.dx), bw["dx"], bf16_out=True)
+            gemm_close(to_f64(lay.dw), bw["dw"], bf16_out=False)
+        g_up.replay()
+        torch.cuda.synchronize()
+        h, s, si = oracle.scale_update(h, s, si, [0, 0, 1], 0)
+        assert _same(lay.hist.cpu().numpy(), h) and _same(lay.scale.cpu().numpy(), s)
+        assert _same(lay.scale_inv.cpu().numpy(), si)
