@@ -19,7 +19,9 @@ Also reported (own timings, HIP events on the launch stream):
   * the lazy transpose-cache fill of the FP8 weight [18432, 12288], cold (GB/s);
   * the FP8-output GEMM (E5M2 output, own scale, amax capture) at the dgrad shape, against the
     bfloat16-output GEMM on the same operands;
-  * the CPU oracle on a bounded sample of the same step (baseline only).
+  * a plain 1 GiB device copy, cold: the box's own streaming ceiling for the cast kernels;
+  * the CPU oracle on a bounded sample of the same step, one thread and all host cores
+    (baseline only).
 """
 from __future__ import annotations
 
@@ -385,6 +387,15 @@ def extras(F, S, torch, np, dev, bf16):
     out["chunked_gemm_8192x12288x12288"] = res
     del A8, B8, D
 
+    # the box's own streaming ceiling: a plain 1 GiB device copy (torch copy_), cold
+    src = torch.empty(1 << 30, **u8).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ms = cold_time(lambda: dst.copy_(src))
+    gbps = 2 * (1 << 30) / (ms * 1e-3) / 1e9
+    out["copy_1GiB_cold"] = {"us": round(ms * 1e3, 1), "GBps": round(gbps, 1), "frac_hbm": round(gbps * 1e9 / HBM_PEAK, 3)}
+    del src, dst
+
     # lazy transpose-cache fill of the FP8 weight [18432, 12288], cold (1 B read + 1 B written)
     Rw, Cw = 18432, 12288
     W8 = torch.randint(0, 256, (Rw, Cw), generator=torch.Generator().manual_seed(9), dtype=torch.uint8).to(dev)
@@ -427,17 +438,34 @@ def cpu_baseline(x_h, w_h, b_h, dy_h):
     rows = 16
     xs = np.ascontiguousarray(x_h[:rows])
     dys = np.ascontiguousarray(dy_h[:rows])
-    with threadpool_limits(limits=1):
+
+    def one_step():
         t = time.perf_counter()
         f = oracle.linear_fwd(xs, w_h, b_h, 1.0, 1.0)
         bw = oracle.linear_bwd(dys, 1.0, f["x8t"], f["x_sinv"], f["w8t"], f["w_sinv"])
         h = np.zeros((HIST_L, 3), np.float32)
         h[0] = [f["x_amax"], f["w_amax"], bw["dy_amax"]]
         oracle.scale_update(h, np.ones(3, np.float32), np.ones(3, np.float32), [0, 0, 1], 0)
-        sec = time.perf_counter() - t
+        return time.perf_counter() - t
+
+    with threadpool_limits(limits=1):
+        sec = one_step()
+    # the same sample with the float64 products on every host core the process may use (the
+    # scalar C parts of the oracle stay single-threaded)
+    ncores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    with threadpool_limits(limits=ncores):
+        sec_all = one_step()
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     flop = 3 * 2.0 * rows * N * K
     return {"value": round(flop / sec / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
             "seconds": round(sec, 2),
+            "all_cores": {"value": round(flop / sec_all / 1e12, 6), "cores": ncores, "seconds": round(sec_all, 2)},
+            "cpu_model": model,
             "sample": f"one training step on {rows} of the {M} token rows of x and dy with the full "
                       f"[{N},{K}] weight (W cast+transpose, three float64 GEMMs, dbias, scale update); "
                       f"FLOPs counted as 3 x 2 x {rows} x {N} x {K}"}

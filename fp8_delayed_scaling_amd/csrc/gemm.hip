@@ -30,6 +30,8 @@
 //
 // k_gemm_bias (any K % 16 == 0): global -> registers -> LDS with double-buffered 128-byte K
 // slices, the K tail zero-filled.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -248,6 +250,10 @@ __device__ __forceinline__ void epilogue_staged(const f32x16 (&acc)[4][4], const
     } else {
         // FP8: 128 rows x 128 bytes = 16 KB; row r at r * 128, 4-byte slot s (columns 4 s ..
         // 4 s + 3) stored at slot s ^ (r & 31).
+        // Pass 1: the amax.  Unsigned order of magnitude bit patterns is numeric order with NaN
+        // above inf, so the wave's amax also says whether any value is NaN.  Pass 2 recomputes
+        // the values and, unless a NaN or a non-plain scale makes a scaled value NaN, encodes
+        // them with the clamp + hardware conversion alone (one wave-uniform branch).
         constexpr int F = OUT - 2;
         const float ds = *oq.scale;
         uint32_t amag = 0;
@@ -258,20 +264,42 @@ __device__ __forceinline__ void epilogue_staged(const f32x16 (&acc)[4][4], const
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r = i * 32 + frow, sl = j * 8 + q * 2 + fhalf;
-                    float v[4];
+                for (int q = 0; q < 4; ++q)
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        v[u] = dequant_bias(acc[i][j][q * 4 + u], sa, sb, bv[q][u]);
-                        amag = max(amag, __float_as_uint(v[u]) & 0x7FFFFFFFu);
-                    }
-                    const uint32_t w = encode4<F>(v[0] * ds, v[1] * ds, v[2] * ds, v[3] * ds);
-                    *reinterpret_cast<uint32_t *>(wlds + r * 128 + ((sl ^ (r & 31)) << 2)) = w;
-                }
+                    for (int u = 0; u < 4; ++u)
+                        amag = max(amag, __float_as_uint(dequant_bias(acc[i][j][q * 4 + u], sa, sb, bv[q][u])) &
+                                             0x7FFFFFFFu);
         }
-        amag = wave_max_u32(amag);
+        amag = __builtin_amdgcn_readfirstlane(wave_max_u32(amag));   // wave-uniform
         if (lane == 0) fold_amax_bits(oq.amax, amag);
+        auto stage = [&](auto fast_tag) {
+            constexpr bool kFast = decltype(fast_tag)::value;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float bv[4][4];
+                load_bias(j, bv);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int r = i * 32 + frow, sl = j * 8 + q * 2 + fhalf;
+                        float y[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) y[u] = dequant_bias(acc[i][j][q * 4 + u], sa, sb, bv[q][u]) * ds;
+                        uint32_t w;
+                        if constexpr (kFast)
+                            w = pack4<F>(clamp_fmt<F>(y[0]), clamp_fmt<F>(y[1]), clamp_fmt<F>(y[2]), clamp_fmt<F>(y[3]));
+                        else
+                            w = encode_exact<F>(y[0]) | (encode_exact<F>(y[1]) << 8) | (encode_exact<F>(y[2]) << 16) |
+                                (encode_exact<F>(y[3]) << 24);
+                        *reinterpret_cast<uint32_t *>(wlds + r * 128 + ((sl ^ (r & 31)) << 2)) = w;
+                    }
+            }
+        };
+        if (scale_is_plain(ds) && amag <= 0x7F800000u)
+            stage(std::true_type{});
+        else
+            stage(std::false_type{});
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_wave_barrier();
         // 16-byte chunk ch of row r = slots 4 ch .. 4 ch + 3, stored in the aligned group
