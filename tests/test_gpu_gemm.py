@@ -104,7 +104,7 @@ def _full_config(M, N, K, fa, fb, seed_base, stdA, stdB, scaleA, scaleB):
 @pytest.mark.parametrize("which", ["fwd", "dgrad", "wgrad"])
 def test_gemm_full_size_qkv_sampled(which):
     """The GPT-175B QKV projection at one TP=2 rank's share (M=8192, K=12288, N=18432) in the
-    launch configuration the benchmark times, checked on 16 seeded full rows and 16 seeded full
+    launch configuration the benchmark times, checked on 64 seeded full rows and 64 seeded full
     columns of the output against the float64 oracle."""
     M, K, N = 8192, 12288, 18432
     if which == "fwd":
@@ -121,8 +121,8 @@ def test_gemm_full_size_qkv_sampled(which):
     D = torch.empty((m, n), device=DEV, dtype=torch.bfloat16)
     F.fp8_gemm_bias(_u8(A8), fa, scalar(1.0), _u8(B8), fb, scalar(1.0 / 64.0), None if bias is None else bf16_dev(bias), D)
     torch.cuda.synchronize()
-    rows = (S.uniform(S.seed_for(4, 13), 0, 16) * m).astype(np.int64)
-    cols = (S.uniform(S.seed_for(4, 14), 0, 16) * n).astype(np.int64)
+    rows = (S.uniform(S.seed_for(4, 13), 0, 64) * m).astype(np.int64)
+    cols = (S.uniform(S.seed_for(4, 14), 0, 64) * n).astype(np.int64)
     Rr, Rc = oracle.gemm_bias_sampled(A8, fa, 1.0, B8, fb, 1.0 / 64.0, bias, rows, cols)
     Dh = to_f64(D)
     big = max(float(np.abs(Rr).max()), float(np.abs(Rc).max()))
@@ -160,11 +160,16 @@ def test_chunked_equals_unchunked_and_graph(n_chunks):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(G.view(torch.int16), ref.view(torch.int16))
-    # sampled oracle check of the chunked output
-    rows = (S.uniform(S.seed_for(5, 3), 0, 8) * M).astype(np.int64)
-    Rr, _ = oracle.gemm_bias_sampled(A8.cpu().numpy(), 0, 1.0, B8.cpu().numpy(), 0, 1.0 / 64,
-                                     S.normal_bf16(S.seed_for(5, 2), (N,), 0.1), rows, [0])
-    gemm_close(to_f64(G)[rows], Rr, bf16_out=True)
+    # sampled oracle check of the chunked output: 64 full rows and 64 full columns, the columns
+    # drawn across every chunk
+    rows = (S.uniform(S.seed_for(5, 3), 0, 64) * M).astype(np.int64)
+    cols = (S.uniform(S.seed_for(5, 4), 0, 64) * N).astype(np.int64)
+    Rr, Rc = oracle.gemm_bias_sampled(A8.cpu().numpy(), 0, 1.0, B8.cpu().numpy(), 0, 1.0 / 64,
+                                      S.normal_bf16(S.seed_for(5, 2), (N,), 0.1), rows, cols)
+    Gh = to_f64(G)
+    big = max(float(np.abs(Rr).max()), float(np.abs(Rc).max()))
+    gemm_close(Gh[rows], Rr, bf16_out=True, scale_ref=big)
+    gemm_close(Gh[:, cols], Rc, bf16_out=True, scale_ref=big)
 
 
 def test_chunked_single_stream_and_ragged_chunks():
