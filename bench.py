@@ -372,8 +372,21 @@ def extras(F, S, torch, np, dev, bf16):
         g.replay()
     torch.cuda.synchronize()
     graph_us = (time.perf_counter() - t) / 200 * 1e6
+    # the same call through the C ABI directly with its arguments marshalled once (what a C
+    # caller pays per call; the difference is the Python binding's argument checks)
+    L = F.lib()
+    raw_args = [xs.data_ptr(), wsm.data_ptr(), bs.data_ptr(), Ms, Ns, Ks, ss[0:1].data_ptr(), hs[0, 0:1].data_ptr(),
+                x8s.data_ptr(), None, sis[0:1].data_ptr(), ss[1:2].data_ptr(), hs[0, 1:2].data_ptr(), w8s.data_ptr(),
+                w8ts.data_ptr(), sis[1:2].data_ptr(), None, ys.data_ptr(), torch.cuda.current_stream().cuda_stream]
+    assert L.fp8_linear_fwd(*raw_args) == 0
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(200):
+        L.fp8_linear_fwd(*raw_args)
+    torch.cuda.synchronize()
+    raw_us = (time.perf_counter() - t) / 200 * 1e6
     out["small_forward_128x256x256"] = {"eager_us_per_call": round(eager_us, 2), "graph_replay_us": round(graph_us, 2),
-                                        "launches": 3}
+                                        "c_abi_eager_us_per_call": round(raw_us, 2), "launches": 3}
 
     # N-chunked GEMM + bias, M=8192, K=N=12288, one stream per chunk, captured as one graph
     Mc, Kc, Nc = 8192, 12288, 12288

@@ -140,12 +140,11 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], const float 
 // r * 512, 16-byte slot s at s ^ (r & 31).  Where D or ldd is not 16-byte aligned, or at the
 // ragged right edge, the elements are stored one by one.
 template <int OUT>
-__device__ __forceinline__ void epilogue_staged(const f32x16 (&acc)[4][4], const float *__restrict__ a_sinv,
-                                                const float *__restrict__ b_sinv, const uint16_t *__restrict__ bias,
-                                                void *__restrict__ D, int64_t ldd, int M, int N, int row0, int col0,
-                                                int lane, uint8_t *wlds, OutQuant oq) {
+__device__ __forceinline__ void epilogue_staged(const f32x16 (&acc)[4][4], float sa, float sb, float ds,
+                                                const uint16_t *__restrict__ bias, void *__restrict__ D, int64_t ldd,
+                                                int M, int N, int row0, int col0, int lane, uint8_t *wlds,
+                                                OutQuant oq) {
     const int frow = lane & 31, fhalf = lane >> 5;
-    const float sa = *a_sinv, sb = *b_sinv;
     constexpr int kElemsPer16 = OUT == 0 ? 8 : OUT == 1 ? 4 : 16;
     const bool vec_ok = ((reinterpret_cast<uintptr_t>(D) & 15u) == 0) && (ldd % kElemsPer16 == 0);
     // bias of the 16 columns this lane holds in column block j.  Columns past N read bias[N - 1]:
@@ -255,7 +254,6 @@ __device__ __forceinline__ void epilogue_staged(const f32x16 (&acc)[4][4], const
         // the values and, unless a NaN or a non-plain scale makes a scaled value NaN, encodes
         // them with the clamp + hardware conversion alone (one wave-uniform branch).
         constexpr int F = OUT - 2;
-        const float ds = *oq.scale;
         uint32_t amag = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -477,6 +475,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias_pipe(const uint8_t *_
                                                                 int K, int tiles_m, int tiles_n, OutQuant oq) {
     if constexpr (OUT >= 2)
         if (blockIdx.x == 0 && threadIdx.x == 0 && oq.scale_inv_out != nullptr) *oq.scale_inv_out = 1.0f / *oq.scale;
+    // scalars the epilogue needs, read before the K loop (uniform: scalar registers)
+    const float sa = *a_sinv, sb = *b_sinv;
+    float ds = 0.f;
+    if constexpr (OUT >= 2) ds = *oq.scale;
     __shared__ __align__(16) uint8_t st0[kPStage];
     __shared__ __align__(16) uint8_t st1[kPStage];
     __shared__ __align__(16) uint8_t st2[kPStage];
@@ -604,7 +606,130 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias_pipe(const uint8_t *_
 #undef FP8DS_STEP
     __syncthreads();   // every wave is done reading the operand stages
     uint8_t *wl = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
-    epilogue_staged<OUT>(acc, a_sinv, b_sinv, bias, D, ldd, M, N, m0 + wm * 128, n0 + wn * 128, lane, wl, oq);
+    epilogue_staged<OUT>(acc, sa, sb, ds, bias, D, ldd, M, N, m0 + wm * 128, n0 + wn * 128, lane, wl, oq);
+}
+
+// ------------------------------------------------------------------------------------------
+// k_gemm_small: problems with fewer than kSmallTiles 256 x 256 tiles (K % 64 == 0).  One wave
+// per 64 x 64 tile, so small outputs still spread over many CUs; each lane loads its own operand
+// fragments straight from global memory into registers, four 64-byte K slices ahead (no LDS,
+// no barriers).  The MFMAs, their operand order and their K order are those of
+// k_gemm_bias_pipe, and so is the epilogue arithmetic, so both kernels give the same bits for
+// every element.
+// ------------------------------------------------------------------------------------------
+constexpr int kSmallTile = 64;
+constexpr int kSmallTiles = 64;   // below this many 256 x 256 tiles the small kernel is used
+
+template <int FA, int FB, int OUT>
+__global__ __launch_bounds__(64) void k_gemm_small(const uint8_t *__restrict__ A, int64_t lda,
+                                                   const uint8_t *__restrict__ B, int64_t ldb,
+                                                   const float *__restrict__ a_sinv, const float *__restrict__ b_sinv,
+                                                   const uint16_t *__restrict__ bias, void *__restrict__ D, int64_t ldd,
+                                                   int M, int N, int K, int tiles_n, OutQuant oq) {
+    if constexpr (OUT >= 2)
+        if (blockIdx.x == 0 && threadIdx.x == 0 && oq.scale_inv_out != nullptr) *oq.scale_inv_out = 1.0f / *oq.scale;
+    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - (blockIdx.x / tiles_n) * tiles_n;
+    const int m0 = tm * kSmallTile, n0 = tn * kSmallTile;
+    const int lane = threadIdx.x, frow = lane & 31, fhalf = lane >> 5;
+    // lane l supplies row l % 32 of each 32-row operand tile and bytes [32 (l / 32), +32) of the
+    // slice; rows past M / N read the last row (their values are never stored or counted)
+    const uint8_t *pa[2], *pb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        pa[i] = A + (int64_t)min(m0 + i * 32 + frow, M - 1) * lda + fhalf * 32;
+        pb[i] = B + (int64_t)min(n0 + i * 32 + frow, N - 1) * ldb + fhalf * 32;
+    }
+    auto ld32 = [](const uint8_t *p) -> i32x8 {
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(p);
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(p + 16);
+        i32x8 r;
+        r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+        r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+        return r;
+    };
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    // the inverse scales, output scale and bias are read before the K loop, so their latency
+    // overlaps the operand loads; bias columns past N read bias[N - 1] (never stored)
+    const float sa = *a_sinv, sb = *b_sinv;
+    float ds = 0.f;
+    if constexpr (OUT >= 2) ds = *oq.scale;
+    float bv[2][4][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int col = min(n0 + j * 32 + q * 8 + fhalf * 4 + u, N - 1);
+                bv[j][q][u] = bias != nullptr ? __uint_as_float((uint32_t)bias[col] << 16) : 0.f;
+            }
+    const int nk = K / kPK;
+#define FP8DS_SLOAD(FA_, FB_, kt)                                                                          \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                                       \
+        FA_[i] = ld32(pa[i] + (int64_t)(kt) * kPK);                                                       \
+        FB_[i] = ld32(pb[i] + (int64_t)(kt) * kPK);                                                       \
+    }
+#define FP8DS_SMFMA(FA_, FB_)                                                                              \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i)                                                         \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                         \
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(FB_[j], FA_[i], acc[i][j], FB, FA, 0, 0, 0, 0);
+    i32x8 a0[2], b0[2], a1[2], b1[2], a2[2], b2[2], a3[2], b3[2];
+    FP8DS_SLOAD(a0, b0, 0)
+    if (nk > 1) { FP8DS_SLOAD(a1, b1, 1) }
+    if (nk > 2) { FP8DS_SLOAD(a2, b2, 2) }
+    if (nk > 3) { FP8DS_SLOAD(a3, b3, 3) }
+    int kt = 0;
+    for (; kt + 4 <= nk; kt += 4) {
+        FP8DS_SMFMA(a0, b0)
+        if (kt + 4 < nk) { FP8DS_SLOAD(a0, b0, kt + 4) }
+        FP8DS_SMFMA(a1, b1)
+        if (kt + 5 < nk) { FP8DS_SLOAD(a1, b1, kt + 5) }
+        FP8DS_SMFMA(a2, b2)
+        if (kt + 6 < nk) { FP8DS_SLOAD(a2, b2, kt + 6) }
+        FP8DS_SMFMA(a3, b3)
+        if (kt + 7 < nk) { FP8DS_SLOAD(a3, b3, kt + 7) }
+    }
+    // the last nk % 4 slices, already in a0, a1, a2 in K order
+    if (kt < nk) { FP8DS_SMFMA(a0, b0) }
+    if (kt + 1 < nk) { FP8DS_SMFMA(a1, b1) }
+    if (kt + 2 < nk) { FP8DS_SMFMA(a2, b2) }
+#undef FP8DS_SLOAD
+#undef FP8DS_SMFMA
+    // epilogue, element by element: lane l holds D[m0 + 32 i + l % 32][n0 + 32 j + 8 (e / 4) +
+    // 4 (l / 32) + e % 4] in element e of acc[i][j]
+    uint32_t amag = 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = m0 + i * 32 + frow;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int col = n0 + j * 32 + (e >> 2) * 8 + fhalf * 4 + (e & 3);
+                const float v = dequant_bias(acc[i][j][e], sa, sb, bv[j][e >> 2][e & 3]);
+                if (row < M && col < N) {
+                    const int64_t o = (int64_t)row * ldd + col;
+                    if constexpr (OUT == 0) {
+                        reinterpret_cast<uint16_t *>(D)[o] = f32_to_bf16_rne(v);
+                    } else if constexpr (OUT == 1) {
+                        reinterpret_cast<float *>(D)[o] = v;
+                    } else {
+                        amag = max(amag, __float_as_uint(v) & 0x7FFFFFFFu);
+                        reinterpret_cast<uint8_t *>(D)[o] = (uint8_t)encode_exact<OUT - 2>(v * ds);
+                    }
+                }
+            }
+    }
+    if constexpr (OUT >= 2) {
+        amag = wave_max_u32(amag);
+        if (lane == 0) fold_amax_bits(oq.amax, amag);
+    }
 }
 
 // D = bias broadcast (K == 0): no products at all.
@@ -661,9 +786,15 @@ hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
     dim3 grid((unsigned)(tiles_m * tiles_n));
     const bool pipe = (K % kPK) == 0;
+    const bool small = pipe && (int64_t)tiles_m * tiles_n < kSmallTiles;
+    const int stiles_n = (int)((N + kSmallTile - 1) / kSmallTile);
+    dim3 sgrid((unsigned)(((M + kSmallTile - 1) / kSmallTile) * stiles_n));
 #define FP8DS_GEMM(FA_, FB_, O_)                                                                           \
     do {                                                                                                   \
-        if (pipe)                                                                                          \
+        if (small)                                                                                         \
+            k_gemm_small<FA_, FB_, O_><<<sgrid, dim3(64), 0, st>>>(                                        \
+                A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, stiles_n, oq);       \
+        else if (pipe)                                                                                     \
             k_gemm_bias_pipe<FA_, FB_, O_><<<grid, dim3(kThreads), 0, st>>>(                               \
                 A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, tiles_m, tiles_n, oq); \
         else                                                                                               \

@@ -185,6 +185,29 @@ def test_chunked_single_stream_and_ragged_chunks():
         assert torch.equal(D.view(torch.int32), ref.view(torch.int32)), n_chunks
 
 
+@pytest.mark.parametrize("out_dtype", [0, 1])
+@pytest.mark.parametrize("shape", [(256, 16384, 512), (300, 16384, 320), (2048, 2048, 1024)])
+def test_small_problem_kernel_matches_large_tile_kernel(shape, out_dtype):
+    """Below 64 tiles of 256 x 256 the GEMM runs a one-wave 64 x 64 tile kernel.  These outputs
+    have exactly 64 large tiles (large-tile kernel); each of their 8 N-chunks has 8 (small
+    kernel).  The MFMA sequence per element is the same, so the chunked output must equal the
+    unchunked one bit for bit, ragged rows included."""
+    M, N, K = shape
+    print(f"small vs large kernel M={M} N={N} K={K} out={out_dtype}", flush=True)
+    A8 = _codes(S.seed_for(24, 0), (M, K), 1, 1.0)
+    B8 = _codes(S.seed_for(24, 1), (N, K), 0, 0.5)
+    bias = S.normal_bf16(S.seed_for(24, 2), (N,), 0.3)
+    ref = _run(A8, 1, 0.5, B8, 0, 0.25, bias, out_dtype)
+    D = torch.zeros_like(ref)
+    F.fp8_gemm_bias_chunked(_u8(A8), 1, scalar(0.5), _u8(B8), 0, scalar(0.25), bf16_dev(bias), D, 8, None)
+    torch.cuda.synchronize()
+    w = torch.int16 if out_dtype == 0 else torch.int32
+    assert torch.equal(D.view(w), ref.view(w))
+    rows = (S.uniform(S.seed_for(24, 3), 0, 8) * M).astype(np.int64)
+    Rr, _ = oracle.gemm_bias_sampled(A8, 1, 0.5, B8, 0, 0.25, bias, rows, [0])
+    gemm_close(to_f64(D)[rows], Rr, bf16_out=(out_dtype == 0))
+
+
 @pytest.mark.parametrize("shape", [(1, 1, 64), (100, 300, 128), (257, 513, 192), (256, 256, 448), (300, 700, 512),
                                    (513, 1000, 576)])
 @pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0)])
