@@ -63,13 +63,17 @@ int check_gemm(const uint8_t *A, int fa, const float *a_sinv, int64_t lda, const
 }
 
 // Events for the chunked GEMM's fork / join, created once per device on first use and kept
-// for the life of the process (event objects, not device memory).
+// for the life of the process (event objects, not device memory).  A stream waits on the
+// event's most recent record at the time of the wait call, so one call's whole record / wait
+// sequence is enqueued under the device's lock: concurrent host threads cannot interleave
+// their records with another call's waits.
 constexpr int kMaxChunks = 16;
 constexpr int kMaxDevices = 64;
 struct ChunkEvents {
     hipEvent_t fork = nullptr;
     hipEvent_t join[kMaxChunks] = {};
     bool ready = false;
+    std::mutex mu;   // held while a chunked call enqueues its records, waits and launches
 };
 ChunkEvents g_events[kMaxDevices];
 std::mutex g_events_mu;
@@ -219,9 +223,11 @@ int fp8_gemm_bias_chunked(const uint8_t *A, int fa, const float *a_scale_inv, in
     int64_t nc = (N + n_chunks - 1) / n_chunks;
     nc = (nc + 15) / 16 * 16;   // chunk starts stay 16-byte aligned in D for both dtypes
     ChunkEvents *ev = nullptr;
+    std::unique_lock<std::mutex> seq;
     if (chunk_streams != nullptr) {
         st = chunk_events(&ev);
         if (st != FP8DS_OK) return st;
+        seq = std::unique_lock<std::mutex>(ev->mu);
         if (hipEventRecord(ev->fork, stream) != hipSuccess) return FP8DS_ERR_HIP;
     }
     for (int c = 0; c < n_chunks; ++c) {

@@ -177,7 +177,10 @@ int fp8_gemm_bias(const uint8_t *A, int fa, const float *a_scale_inv, int64_t ld
  * chunk_streams[c] (HOST array of n_chunks streams), ordered after the work already queued on
  * `stream` and joined back into `stream` with events, so the whole sequence can be captured
  * from `stream` as one hipGraph.  1 <= n_chunks <= 16.  The output equals fp8_gemm_bias bit for
- * bit.  chunk_streams may be NULL: then all chunks run on `stream` in order.
+ * bit.  chunk_streams may be NULL: then all chunks run on `stream` in order.  The fork / join
+ * events are the library's own (created once per device, kept for the process); each call
+ * enqueues its records and waits under a per-device lock, so several host threads may call
+ * this at once.
  */
 int fp8_gemm_bias_chunked(const uint8_t *A, int fa, const float *a_scale_inv, int64_t lda,
                           const uint8_t *B, int fb, const float *b_scale_inv, int64_t ldb,

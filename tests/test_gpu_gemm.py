@@ -185,6 +185,49 @@ def test_chunked_single_stream_and_ragged_chunks():
         assert torch.equal(D.view(torch.int32), ref.view(torch.int32)), n_chunks
 
 
+def test_chunked_from_several_host_threads():
+    """Four host threads each enqueue chunked GEMMs on their own streams at the same time (the
+    ctypes calls release the interpreter lock); the shared fork / join events must keep every
+    call's chunks ordered after its own inputs and joined into its own stream."""
+    import threading
+    M, N, K = 512, 3072, 512
+    A8 = _u8(_codes(S.seed_for(25, 0), (M, K), 0, 1.0))
+    B8 = _u8(_codes(S.seed_for(25, 1), (N, K), 0, 1.0))
+    bias = bf16_dev(S.normal_bf16(S.seed_for(25, 2), (N,), 0.2))
+    sa, sb = scalar(0.5), scalar(0.5)
+    ref = torch.empty((M, N), device=DEV, dtype=torch.float32)
+    F.fp8_gemm_bias(A8, 0, sa, B8, 0, sb, bias, ref)
+    torch.cuda.synchronize()
+    nthreads, ncalls = 4, 6
+    outs = [[torch.full((M, N), float("nan"), device=DEV) for _ in range(ncalls)] for _ in range(nthreads)]
+    errors = []
+
+    def worker(t):
+        try:
+            main = torch.cuda.Stream()
+            streams = [torch.cuda.Stream() for _ in range(4)]
+            for c in range(ncalls):
+                # the output is cleared on the caller's stream just before the call, so a chunk that
+                # is not ordered after that clear can be overwritten by it
+                with torch.cuda.stream(main):
+                    outs[t][c].zero_()
+                F.fp8_gemm_bias_chunked(A8, 0, sa, B8, 0, sb, bias, outs[t][c], 4, streams, stream=main)
+            main.synchronize()
+        except Exception as e:   # reported below
+            errors.append(e)
+
+    th = [threading.Thread(target=worker, args=(t,)) for t in range(nthreads)]
+    for x in th:
+        x.start()
+    for x in th:
+        x.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for t in range(nthreads):
+        for c in range(ncalls):
+            assert torch.equal(outs[t][c].view(torch.int32), ref.view(torch.int32)), (t, c)
+
+
 @pytest.mark.parametrize("out_dtype", [0, 1])
 @pytest.mark.parametrize("shape", [(256, 16384, 512), (300, 16384, 320), (2048, 2048, 1024)])
 def test_small_problem_kernel_matches_large_tile_kernel(shape, out_dtype):
