@@ -91,7 +91,7 @@ def main():
         traffic_probe()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
+        print(json.dumps({"error": "this benchmark runs on one GPU only; sharding across GPUs is described, "
                                    "not implemented (run with --gpus 1)"}))
         sys.exit(2)
 
