@@ -386,7 +386,7 @@ def extras(F, S, torch, np, dev, bf16):
     torch.cuda.synchronize()
     raw_us = (time.perf_counter() - t) / 200 * 1e6
     out["small_forward_128x256x256"] = {"eager_us_per_call": round(eager_us, 2), "graph_replay_us": round(graph_us, 2),
-                                        "c_abi_eager_us_per_call": round(raw_us, 2), "launches": 3}
+                                        "c_abi_eager_us_per_call": round(raw_us, 2), "launches": 2}
 
     # N-chunked GEMM + bias, M=8192, K=N=12288, one stream per chunk, captured as one graph
     Mc, Kc, Nc = 8192, 12288, 12288

@@ -270,14 +270,10 @@ int fp8_linear_fwd(const uint16_t *x, const uint16_t *w, const uint16_t *bias, i
                     N, K);
     if (st != FP8DS_OK) return st;
     if (K > 0) {
-        hipError_t e = x8_t != nullptr
-                           ? fp8ds::launch_cast_transpose(x, M, K, x_scale, FP8DS_E4M3, x8, x8_t, x_scale_inv,
-                                                          x_amax, nullptr, stream)
-                           : fp8ds::launch_cast_amax(x, M * K, x_scale, FP8DS_E4M3, x8, x_scale_inv, x_amax, nullptr,
-                                                     stream);
-        if (e != hipSuccess) return FP8DS_ERR_HIP;
-        e = fp8ds::launch_cast_transpose(w, N, K, w_scale, FP8DS_E4M3, w8, w8_t, w_scale_inv, w_amax, w_noop,
-                                         stream);
+        // x (with or without its transpose) and W in one launch
+        hipError_t e = fp8ds::launch_cast_transpose_pair(x, M, K, x_scale, x8, x8_t, x_scale_inv, x_amax, nullptr,
+                                                         w, N, K, w_scale, w8, w8_t, w_scale_inv, w_amax, w_noop,
+                                                         FP8DS_E4M3, stream);
         if (e != hipSuccess) return FP8DS_ERR_HIP;
     }
     return hip_status(fp8ds::launch_gemm_bias(x8, FP8DS_E4M3, x_scale_inv, K, w8, FP8DS_E4M3, w_scale_inv, K, bias,

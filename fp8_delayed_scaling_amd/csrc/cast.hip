@@ -118,23 +118,41 @@ constexpr int kCtThreads = (kTile / 8) * (kTileC / 8);   // 512
 // swapped when g is odd.
 __device__ __forceinline__ int t_swz(int col) { return (col >> 3) & 15; }
 
+// One tensor of a cast launch.  out_t == nullptr: row-major codes only (no transpose cache).
+struct CtTensor {
+    const uint16_t *x;
+    int64_t rows, cols;
+    const float *scale;
+    uint8_t *out, *out_t;
+    float *sinv_out, *amax_slot;
+    const float *noop;
+};
+// Up to two tensors cast by one launch (the forward pass casts x and W together): blocks
+// [0, first1) take tiles of t[0], blocks [first1, ...) tiles of t[1].
+struct CtBatch {
+    CtTensor t[2];
+    int64_t first1;
+};
+
 template <int FMT, bool VEC, bool DBIAS>
-__global__ __launch_bounds__(kCtThreads) void k_cast_transpose(const uint16_t *__restrict__ x, int64_t rows,
-                                                        int64_t cols, const float *__restrict__ scale_p,
-                                                        uint8_t *__restrict__ out, uint8_t *__restrict__ out_t,
-                                                        float *__restrict__ sinv_out, float *amax_slot,
-                                                        const float *__restrict__ noop,
-                                                        float *__restrict__ partial) {
+__global__ __launch_bounds__(kCtThreads) void k_cast_transpose(const CtBatch batch, float *__restrict__ partial) {
     __shared__ __align__(16) uint8_t tT[kTileC * kTile];
     __shared__ float csum[DBIAS ? 16 * kTileC : 1];
     __shared__ uint32_t red[kCtThreads / 64];
-    if (noop != nullptr && *noop == 1.0f) return;
+    const bool second = (int64_t)blockIdx.x >= batch.first1;
+    const CtTensor &T = second ? batch.t[1] : batch.t[0];
+    const uint16_t *__restrict__ x = T.x;
+    const int64_t rows = T.rows, cols = T.cols;
+    uint8_t *__restrict__ out = T.out;
+    uint8_t *__restrict__ out_t = T.out_t;
+    if (T.noop != nullptr && *T.noop == 1.0f) return;
 
-    const float s = *scale_p;
+    const float s = *T.scale;
     const int t = threadIdx.x;
     const int rb = t >> 5, cb = t & 31;
+    const int64_t block = (int64_t)blockIdx.x - (second ? batch.first1 : 0);
     const int64_t tiles_c = (cols + kTileC - 1) / kTileC;
-    const int64_t tile_r = blockIdx.x / tiles_c, tile_c = blockIdx.x - tile_r * tiles_c;
+    const int64_t tile_r = block / tiles_c, tile_c = block - tile_r * tiles_c;
     const int64_t r0 = tile_r * kTile;
     const int64_t c0 = tile_c * kTileC;
     const int64_t row = r0 + rb * 8;   // first row of the micro-tile
@@ -234,7 +252,9 @@ __global__ __launch_bounds__(kCtThreads) void k_cast_transpose(const uint16_t *_
         }
     }
 
+    const bool want_t = out_t != nullptr;   // block-uniform
     // ---- transposed fragments into LDS: T[cb*8 + c][rb*8 .. rb*8+7]
+    if (want_t)
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         const int tc = cb * 8 + c;
@@ -265,6 +285,7 @@ __global__ __launch_bounds__(kCtThreads) void k_cast_transpose(const uint16_t *_
     __syncthreads();
 
     // ---- transposed tile out: 256 transposed rows x 128 bytes, 16-byte chunks
+    if (want_t)
 #pragma unroll
     for (int i = 0; i < (kTileC * kTile / 16) / kCtThreads; ++i) {
         const int q = t + kCtThreads * i;
@@ -300,8 +321,8 @@ __global__ __launch_bounds__(kCtThreads) void k_cast_transpose(const uint16_t *_
     // ---- amax: one atomic per block; inverse scale from block (0, 0)
     uint32_t bm = block_max_u32<kCtThreads>(mag, red);
     if (t == 0) {
-        fold_amax(amax_slot, bm);
-        if (blockIdx.x == 0 && sinv_out != nullptr) *sinv_out = 1.0f / s;
+        fold_amax(T.amax_slot, bm);
+        if (block == 0 && T.sinv_out != nullptr) *T.sinv_out = 1.0f / s;
     }
 }
 
@@ -339,14 +360,15 @@ hipError_t launch_cast_amax(const uint16_t *x, int64_t n, const float *scale, in
     return hipGetLastError();
 }
 
+static int64_t ct_tiles(int64_t rows, int64_t cols) {
+    return ((cols + kTileC - 1) / kTileC) * ((rows + kTile - 1) / kTile);
+}
+static bool ct_vec(int64_t rows, int64_t cols) { return (cols % 8 == 0) && (rows % 16 == 0); }
+
 template <bool DBIAS>
-static hipError_t launch_ct(const uint16_t *x, int64_t rows, int64_t cols, const float *scale, int fmt,
-                            uint8_t *out, uint8_t *out_t, float *sinv_out, float *amax_slot,
-                            const float *noop, float *partial, hipStream_t st) {
-    dim3 grid((unsigned)(((cols + kTileC - 1) / kTileC) * ((rows + kTile - 1) / kTile)));
-    const bool vec = (cols % 8 == 0) && (rows % 16 == 0);
-#define FP8DS_CT(F, V) \
-    k_cast_transpose<F, V, DBIAS><<<grid, dim3(kCtThreads), 0, st>>>(x, rows, cols, scale, out, out_t, sinv_out, amax_slot, noop, partial)
+static hipError_t launch_batch(const CtBatch &b, int64_t blocks, bool vec, int fmt, float *partial, hipStream_t st) {
+    dim3 grid((unsigned)blocks);
+#define FP8DS_CT(F, V) k_cast_transpose<F, V, DBIAS><<<grid, dim3(kCtThreads), 0, st>>>(b, partial)
     if (fmt == kE4M3) {
         if (vec) FP8DS_CT(kE4M3, true); else FP8DS_CT(kE4M3, false);
     } else {
@@ -356,11 +378,46 @@ static hipError_t launch_ct(const uint16_t *x, int64_t rows, int64_t cols, const
     return hipGetLastError();
 }
 
+template <bool DBIAS>
+static hipError_t launch_ct(const uint16_t *x, int64_t rows, int64_t cols, const float *scale, int fmt,
+                            uint8_t *out, uint8_t *out_t, float *sinv_out, float *amax_slot,
+                            const float *noop, float *partial, hipStream_t st) {
+    CtBatch b{};
+    b.t[0] = CtTensor{x, rows, cols, scale, out, out_t, sinv_out, amax_slot, noop};
+    b.t[1] = b.t[0];
+    const int64_t n = ct_tiles(rows, cols);
+    b.first1 = n;
+    return launch_batch<DBIAS>(b, n, ct_vec(rows, cols), fmt, partial, st);
+}
+
 hipError_t launch_cast_transpose(const uint16_t *x, int64_t rows, int64_t cols, const float *scale, int fmt,
                                  uint8_t *out, uint8_t *out_t, float *sinv_out, float *amax_slot,
                                  const float *noop, hipStream_t st) {
     if (rows == 0 || cols == 0) return hipSuccess;
     return launch_ct<false>(x, rows, cols, scale, fmt, out, out_t, sinv_out, amax_slot, noop, nullptr, st);
+}
+
+hipError_t launch_cast_transpose_pair(const uint16_t *x0, int64_t rows0, int64_t cols0, const float *scale0,
+                                      uint8_t *out0, uint8_t *out_t0, float *sinv0, float *amax0, const float *noop0,
+                                      const uint16_t *x1, int64_t rows1, int64_t cols1, const float *scale1,
+                                      uint8_t *out1, uint8_t *out_t1, float *sinv1, float *amax1, const float *noop1,
+                                      int fmt, hipStream_t st) {
+    const bool v0 = ct_vec(rows0, cols0), v1 = ct_vec(rows1, cols1);
+    const int64_t n0 = (rows0 == 0 || cols0 == 0) ? 0 : ct_tiles(rows0, cols0);
+    const int64_t n1 = (rows1 == 0 || cols1 == 0) ? 0 : ct_tiles(rows1, cols1);
+    if (v0 != v1 || n0 == 0 || n1 == 0) {
+        // the two tensors need different code paths (or one is empty): one launch each
+        hipError_t e = hipSuccess;
+        if (n0) e = launch_ct<false>(x0, rows0, cols0, scale0, fmt, out0, out_t0, sinv0, amax0, noop0, nullptr, st);
+        if (e == hipSuccess && n1)
+            e = launch_ct<false>(x1, rows1, cols1, scale1, fmt, out1, out_t1, sinv1, amax1, noop1, nullptr, st);
+        return e;
+    }
+    CtBatch b{};
+    b.t[0] = CtTensor{x0, rows0, cols0, scale0, out0, out_t0, sinv0, amax0, noop0};
+    b.t[1] = CtTensor{x1, rows1, cols1, scale1, out1, out_t1, sinv1, amax1, noop1};
+    b.first1 = n0;
+    return launch_batch<false>(b, n0 + n1, v0, fmt, nullptr, st);
 }
 
 size_t dbias_workspace_bytes(int64_t rows, int64_t cols) {

@@ -12,6 +12,13 @@ hipError_t launch_cast_amax(const uint16_t *x, int64_t n, const float *scale, in
 hipError_t launch_cast_transpose(const uint16_t *x, int64_t rows, int64_t cols, const float *scale, int fmt,
                                  uint8_t *out, uint8_t *out_t, float *sinv_out, float *amax_slot,
                                  const float *noop, hipStream_t st);
+// x0 and x1 cast+transposed (out_t may be nullptr: codes only) by one launch when both take the
+// same code path, else by two; one FP8 format for both.
+hipError_t launch_cast_transpose_pair(const uint16_t *x0, int64_t rows0, int64_t cols0, const float *scale0,
+                                      uint8_t *out0, uint8_t *out_t0, float *sinv0, float *amax0, const float *noop0,
+                                      const uint16_t *x1, int64_t rows1, int64_t cols1, const float *scale1,
+                                      uint8_t *out1, uint8_t *out_t1, float *sinv1, float *amax1, const float *noop1,
+                                      int fmt, hipStream_t st);
 size_t dbias_workspace_bytes(int64_t rows, int64_t cols);
 hipError_t launch_dbias_cast_transpose(const uint16_t *dy, int64_t rows, int64_t cols, const float *scale,
                                        int fmt, uint8_t *out, uint8_t *out_t, float *sinv_out,

@@ -384,3 +384,30 @@ def test_weight_caching_across_microbatches_in_a_graph():
         h, s, si = oracle.scale_update(h, s, si, [0, 0, 1], 0)
         assert _same(lay.hist.cpu().numpy(), h) and _same(lay.scale.cpu().numpy(), s)
         assert _same(lay.scale_inv.cpu().numpy(), si)
+
+
+@pytest.mark.parametrize("shape", [(256, 384, 512), (100, 256, 256), (128, 200, 256), (37, 24, 48)])
+@pytest.mark.parametrize("with_xt", [True, False])
+def test_linear_fwd_grouped_casts(shape, with_xt):
+    """fp8_linear_fwd casts x and W in one launch when both take the same code path (rows % 16
+    and cols % 8), else in two; with and without x's transpose cache.  Codes, transposes, amaxes,
+    inverse scales and y against the oracle."""
+    M, N, K = shape
+    print(f"linear fwd grouped casts M={M} N={N} K={K} x_t={with_xt}", flush=True)
+    xh = S.normal_bf16(S.seed_for(8, 0), (M, K), 1.0)
+    wh = S.normal_bf16(S.seed_for(8, 1), (N, K), 0.5)
+    bh = S.normal_bf16(S.seed_for(8, 2), (N,), 0.1)
+    lay = Layer(M, N, K)
+    lay.scale.copy_(torch.tensor([3.0, 24.0, 1.0]))
+    x8t = lay.x8t if with_xt else None
+    F.fp8_linear_fwd(bf16_dev(xh), bf16_dev(wh), bf16_dev(bh), lay.scale[0:1], lay.hist[0, 0:1], lay.x8, x8t,
+                     lay.sinv[0:1], lay.scale[1:2], lay.hist[0, 1:2], lay.w8, lay.w8t, lay.sinv[1:2], None, lay.y)
+    torch.cuda.synchronize()
+    fw = oracle.linear_fwd(xh, wh, bh, 3.0, 24.0, want_x_t=with_xt)
+    assert np.array_equal(u8_host(lay.x8), fw["x8"])
+    if with_xt:
+        assert np.array_equal(u8_host(lay.x8t), fw["x8t"])
+    assert np.array_equal(u8_host(lay.w8), fw["w8"]) and np.array_equal(u8_host(lay.w8t), fw["w8t"])
+    assert _same(lay.hist[0, :2].cpu().numpy(), [fw["x_amax"], fw["w_amax"]])
+    assert _same(lay.sinv[:2].cpu().numpy(), [fw["x_sinv"], fw["w_sinv"]])
+    gemm_close(to_f64(lay.y), fw["y"], bf16_out=True)
