@@ -20,6 +20,8 @@ Also reported (own timings, HIP events on the launch stream):
   * the FP8-output GEMM (E5M2 output, own scale, amax capture) at the dgrad shape, against the
     bfloat16-output GEMM on the same operands;
   * a plain 1 GiB device copy, cold: the box's own streaming ceiling for the cast kernels;
+  * for context only, the vendor library's FP8 GEMM (hipBLASLt via torch._scaled_mm) beside this
+    library's GEMM on the same forward-shape operands;
   * the CPU oracle on a bounded sample of the same step, one thread and all host cores
     (baseline only).
 """
@@ -459,7 +461,30 @@ def extras(F, S, torch, np, dev, bf16):
         tb = min(tb, _time_fn(torch, lambda: F.fp8_gemm_bias(A8, 0, sa, B8, 0, sb, None, Db), 5))
     out["fp8_out_gemm_8192x12288x18432"] = {"fp8_out_tflops": round(flop / (t8 * 1e-3) / 1e12, 1),
                                              "bf16_out_tflops": round(flop / (tb * 1e-3) / 1e12, 1)}
-    del A8, B8, D8, Db, flush
+    del A8, B8, D8, Db
+
+    # context, not a target: the vendor library's FP8 GEMM (hipBLASLt through torch._scaled_mm)
+    # and this library's GEMM on the same forward-shape operands, timed alternately
+    A8, B8 = codes(12, M, K), codes(13, N, K)
+    Yb = torch.empty((M, N), device=dev, dtype=torch.bfloat16)
+    flop = 2.0 * M * N * K
+    try:
+        a8, b8 = A8.view(torch.float8_e4m3fn), B8.view(torch.float8_e4m3fn)
+        one = torch.tensor(1.0, device=dev)
+        lib_call = lambda: torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+        lib_call()
+        F.fp8_gemm_bias(A8, 0, sa, B8, 0, sb, None, Yb)
+        torch.cuda.synchronize()
+        tl = to = float("inf")
+        for _ in range(3):
+            tl = min(tl, _time_fn(torch, lib_call, 5))
+            to = min(to, _time_fn(torch, lambda: F.fp8_gemm_bias(A8, 0, sa, B8, 0, sb, None, Yb), 5))
+        out["vendor_gemm_context_8192x18432x12288"] = {
+            "hipblaslt_scaled_mm_tflops": round(flop / (tl * 1e-3) / 1e12, 1),
+            "fp8ds_gemm_tflops": round(flop / (to * 1e-3) / 1e12, 1)}
+    except Exception as ex:   # the vendor path is context only
+        out["vendor_gemm_context_8192x18432x12288"] = {"error": repr(ex)[:200]}
+    del A8, B8, Yb, flush
     torch.cuda.empty_cache()
     return out
 
