@@ -207,6 +207,49 @@ def test_dbias_deterministic():
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
+@pytest.mark.parametrize("shape", [(2048, 1024), (300, 700), (8192, 4096)])
+def test_dbias_workspace_garbage_reuse_and_graph(shape):
+    """Whatever the workspace holds on entry (random bytes, all ones, zeros), dbias is the same
+    bits, call after call on the same workspace, and on every replay of a captured graph."""
+    R, C = shape
+    print(f"dbias workspace reuse {shape}", flush=True)
+    dyh = S.normal_bf16(S.seed_for(3, 10), (R, C), 0.01)
+    dy = bf16_dev(dyh)
+    out = torch.empty((R, C), dtype=torch.uint8, device=DEV)
+    out_t = torch.empty((C, R), dtype=torch.uint8, device=DEV)
+    nbytes = F.fp8_dbias_workspace_bytes(R, C)
+    ws = torch.empty(nbytes + 64, dtype=torch.uint8, device=DEV)
+    ref = torch.empty((C,), dtype=torch.float32, device=DEV)
+    F.fp8_dbias_cast_transpose(dy, scalar(1.0), F.E5M2, out, out_t, ref, ws)
+    torch.cuda.synchronize()
+    db = oracle.dbias(dyh)
+    assert np.all(np.abs(ref.cpu().numpy() - db) <= 1e-5 * np.abs(S.bf16_bits_to_f64(dyh)).sum(0) + 1e-30)
+    fills = [torch.from_numpy(S.random_bytes(S.seed_for(3, 11), (nbytes + 64,))).to(DEV),
+             torch.full((nbytes + 64,), 0xFF, dtype=torch.uint8, device=DEV),
+             torch.zeros(nbytes + 64, dtype=torch.uint8, device=DEV)]
+    for k, fill in enumerate(fills):
+        ws.copy_(fill)
+        for rep in range(3):
+            got = torch.full((C,), float("nan"), dtype=torch.float32, device=DEV)
+            F.fp8_dbias_cast_transpose(dy, scalar(1.0), F.E5M2, out, out_t, got, ws)
+            torch.cuda.synchronize()
+            assert torch.equal(got.view(torch.int32), ref.view(torch.int32)), (k, rep)
+    # captured once, replayed
+    got = torch.zeros((C,), dtype=torch.float32, device=DEV)
+    one = scalar(1.0)
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cap):
+        F.fp8_dbias_cast_transpose(dy, one, F.E5M2, out, out_t, got, ws, stream=cap)
+    for rep in range(4):
+        got.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int32), ref.view(torch.int32)), rep
+
+
 def test_empty_inputs_launch_nothing():
     x = torch.empty((0,), dtype=torch.bfloat16, device=DEV)
     out = torch.empty((0,), dtype=torch.uint8, device=DEV)
