@@ -252,7 +252,8 @@ def main():
     del evs
 
     if not args.no_extras:
-        result["extras"] = extras(F, S, torch, np, dev, bf16)
+        result["extras"] = extras(F, S, torch, np, dev, bf16,
+                                  {"x8": x8, "w8": w8, "w8t": w8t, "dy8": dy8, "sinv": sinv})
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(x_h, w_h, b_h, dy_h)
@@ -285,7 +286,10 @@ def _time_fn(torch, fn, reps=20):
     return s.elapsed_time(e) / reps
 
 
-def extras(F, S, torch, np, dev, bf16):
+def extras(F, S, torch, np, dev, bf16, step):
+    """Timings beyond the step.  The GEMM extras use the step's own FP8 operands (x8, W8, W8^T,
+    dy8 cast from the normal-distributed inputs at the step's scales): a GEMM's power draw, and
+    with it the clock it runs at, depends on the operands' bits."""
     out = {}
     u8 = dict(device=dev, dtype=torch.uint8)
     f32 = dict(device=dev, dtype=torch.float32)
@@ -390,23 +394,16 @@ def extras(F, S, torch, np, dev, bf16):
     out["small_forward_128x256x256"] = {"eager_us_per_call": round(eager_us, 2), "graph_replay_us": round(graph_us, 2),
                                         "c_abi_eager_us_per_call": round(raw_us, 2), "launches": 2}
 
-    # N-chunked GEMM + bias, M=8192, K=N=12288, one stream per chunk, captured as one graph
+    # N-chunked GEMM + bias, M=8192, K=N=12288 (x8 and the first 12288 rows of W8), one stream
+    # per chunk, captured as one graph
     Mc, Kc, Nc = 8192, 12288, 12288
-    def codes(seed, rows, cols=Kc):
-        """Seeded finite E4M3 codes (exponent field even, so never the NaN code), mixed signs."""
-        c = torch.randint(0, 256, (rows, cols), generator=torch.Generator().manual_seed(seed), dtype=torch.uint8)
-        return (c & 0xF7).to(dev)
-
-    A8 = codes(7, Mc)
-    B8 = codes(8, Nc)
+    A8 = step["x8"]
+    B8 = step["w8"][:Nc]
     biasc = bf16(S.normal_bf16(S.seed_for(5, 2), (Nc,), 0.1))
-    sa, sb = torch.tensor([1.0], **f32), torch.tensor([1.0], **f32)
+    sa, sb = step["sinv"][0:1], step["sinv"][1:2]
     D = torch.empty((Mc, Nc), device=dev, dtype=torch.bfloat16)
     flop = 2.0 * Mc * Nc * Kc
-    F.fp8_gemm_bias(A8, 0, sa, B8, 0, sb, biasc, D)
-    torch.cuda.synchronize()
-    res = {"unchunked_tflops": round(flop / (_time_fn(torch, lambda: F.fp8_gemm_bias(A8, 0, sa, B8, 0, sb, biasc, D), 10)
-                                            * 1e-3) / 1e12, 1)}
+    graphs = {}
     for nch in (4, 8):
         streams = [torch.cuda.Stream() for _ in range(nch)]
         cap = torch.cuda.Stream()
@@ -417,8 +414,18 @@ def extras(F, S, torch, np, dev, bf16):
             F.fp8_gemm_bias_chunked(A8, 0, sa, B8, 0, sb, biasc, D, nch, streams, stream=cap)
         g.replay()
         torch.cuda.synchronize()
-        ms = _time_fn(torch, g.replay, 10)
-        res[f"chunks{nch}_graph_tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
+        graphs[nch] = (g, streams)
+    # three rounds, the three forms alternating; each form's best round
+    best = {"unchunked": float("inf"), 4: float("inf"), 8: float("inf")}
+    for _ in range(3):
+        best["unchunked"] = min(best["unchunked"],
+                                _time_fn(torch, lambda: F.fp8_gemm_bias(A8, 0, sa, B8, 0, sb, biasc, D), 5))
+        for nch in (4, 8):
+            best[nch] = min(best[nch], _time_fn(torch, graphs[nch][0].replay, 5))
+    res = {"unchunked_tflops": round(flop / (best["unchunked"] * 1e-3) / 1e12, 1),
+           "chunks4_graph_tflops": round(flop / (best[4] * 1e-3) / 1e12, 1),
+           "chunks8_graph_tflops": round(flop / (best[8] * 1e-3) / 1e12, 1)}
+    del graphs
     out["chunked_gemm_8192x12288x12288"] = res
     del A8, B8, D
 
@@ -445,33 +452,37 @@ def extras(F, S, torch, np, dev, bf16):
     # GEMM writing an FP8 output with its own scale and amax capture, dgrad shape of the step
     # (M=8192, N=12288, K=18432), against the bfloat16-output GEMM on the same operands
     Mg, Ng, Kg = 8192, 12288, 18432
-    A8, B8 = codes(10, Mg, Kg), codes(11, Ng, Kg)
+    A8, B8 = step["dy8"], step["w8t"]      # the dgrad operands: dy8 [M, N] (E5M2), W8^T [K, N]
+    sa, sb = step["sinv"][2:3], step["sinv"][1:2]
     D8 = torch.empty((Mg, Ng), **u8)
     Db = torch.empty((Mg, Ng), device=dev, dtype=torch.bfloat16)
-    ds, dsi, dam = torch.tensor([1.0 / 4096], **f32), torch.zeros(1, **f32), torch.zeros(1, **f32)
+    # output scale 2^18: dx ~ N(0, 0.027) here, so its amax lands near the top of E5M2's range
+    ds, dsi, dam = torch.tensor([2.0 ** 18], **f32), torch.zeros(1, **f32), torch.zeros(1, **f32)
     flop = 2.0 * Mg * Ng * Kg
-    F.fp8_gemm_bias_fp8(A8, 0, sa, B8, 0, sb, None, D8, F.E5M2, ds, dsi, dam)
-    F.fp8_gemm_bias(A8, 0, sa, B8, 0, sb, None, Db)
+    F.fp8_gemm_bias_fp8(A8, F.E5M2, sa, B8, F.E4M3, sb, None, D8, F.E5M2, ds, dsi, dam)
+    F.fp8_gemm_bias(A8, F.E5M2, sa, B8, F.E4M3, sb, None, Db)
     torch.cuda.synchronize()
     # alternate the two for three rounds and keep each one's best round, so neither is measured
     # alone in a colder or hotter clock state
     t8 = tb = float("inf")
     for _ in range(3):
-        t8 = min(t8, _time_fn(torch, lambda: F.fp8_gemm_bias_fp8(A8, 0, sa, B8, 0, sb, None, D8, F.E5M2, ds, dsi, dam), 5))
-        tb = min(tb, _time_fn(torch, lambda: F.fp8_gemm_bias(A8, 0, sa, B8, 0, sb, None, Db), 5))
+        t8 = min(t8, _time_fn(torch, lambda: F.fp8_gemm_bias_fp8(A8, F.E5M2, sa, B8, F.E4M3, sb, None, D8, F.E5M2,
+                                                                  ds, dsi, dam), 5))
+        tb = min(tb, _time_fn(torch, lambda: F.fp8_gemm_bias(A8, F.E5M2, sa, B8, F.E4M3, sb, None, Db), 5))
     out["fp8_out_gemm_8192x12288x18432"] = {"fp8_out_tflops": round(flop / (t8 * 1e-3) / 1e12, 1),
                                              "bf16_out_tflops": round(flop / (tb * 1e-3) / 1e12, 1)}
-    del A8, B8, D8, Db
+    del D8, Db
 
     # context, not a target: the vendor library's FP8 GEMM (hipBLASLt through torch._scaled_mm)
     # and this library's GEMM on the same forward-shape operands, timed alternately
-    A8, B8 = codes(12, M, K), codes(13, N, K)
+    A8, B8 = step["x8"], step["w8"]        # the forward operands
+    sa, sb = step["sinv"][0:1], step["sinv"][1:2]
     Yb = torch.empty((M, N), device=dev, dtype=torch.bfloat16)
     flop = 2.0 * M * N * K
     try:
         a8, b8 = A8.view(torch.float8_e4m3fn), B8.view(torch.float8_e4m3fn)
-        one = torch.tensor(1.0, device=dev)
-        lib_call = lambda: torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+        lib_call = lambda: torch._scaled_mm(a8, b8.t(), scale_a=step["sinv"][0], scale_b=step["sinv"][1],
+                                            out_dtype=torch.bfloat16)
         lib_call()
         F.fp8_gemm_bias(A8, 0, sa, B8, 0, sb, None, Yb)
         torch.cuda.synchronize()
@@ -484,7 +495,7 @@ def extras(F, S, torch, np, dev, bf16):
             "fp8ds_gemm_tflops": round(flop / (to * 1e-3) / 1e12, 1)}
     except Exception as ex:   # the vendor path is context only
         out["vendor_gemm_context_8192x18432x12288"] = {"error": repr(ex)[:200]}
-    del A8, B8, Yb, flush
+    del Yb, flush
     torch.cuda.empty_cache()
     return out
 
