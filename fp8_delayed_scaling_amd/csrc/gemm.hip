@@ -65,11 +65,15 @@ __device__ __forceinline__ void block_tile(int tiles_m, int tiles_n, int &tm, in
     tn = in_group / gm;
 }
 
+// float32 -> bfloat16, round to nearest even, by the hardware conversion (gfx950 converts two
+// values per instruction).  A NaN stays a NaN; its payload is not specified.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
-    uint32_t u = __float_as_uint(v);
-    if (v != v) return 0x7FC0u;
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float lo, float hi) {
+    const bf16x2_t p = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, p);
 }
 }  // namespace
 
@@ -174,8 +178,7 @@ __device__ __forceinline__ void epilogue_staged(const f32x16 (&acc)[4][4], float
                     float v[4];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) v[u] = dequant_bias(acc[i][j][q * 4 + u], sa, sb, bv[q][u]);
-                    const u32x2 pk = {(uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16),
-                                      (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16)};
+                    const u32x2 pk = {f32x2_to_bf16x2_rne(v[0], v[1]), f32x2_to_bf16x2_rne(v[2], v[3])};
                     *reinterpret_cast<u32x2 *>(wlds + r * 256 + ((sl ^ (r & 31)) << 3)) = pk;
                 }
         }

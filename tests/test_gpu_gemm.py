@@ -272,3 +272,31 @@ def test_gemm_pipelined_path_shapes(shape, fa, fb):
     pad = np.zeros((M, 16), np.uint8), np.zeros((N, 16), np.uint8)
     Dg = _run(np.hstack([A8, pad[0]]), fa, 0.5, np.hstack([B8, pad[1]]), fb, 0.25, bias, 1)
     assert torch.equal(D.view(torch.int32), Dg.view(torch.int32))
+
+
+@pytest.mark.parametrize("sa,sb", [(1.2345678, 1.0), (1.01171875, 1.0), (0.70710677, 2.0 ** -120), (1.9, 2.0 ** 110)])
+@pytest.mark.parametrize("shape", [(256, 64, 64), (1280, 2048, 64), (300, 200, 48)],
+                         ids=["small-kernel", "pipelined-kernel", "general-kernel"])
+def test_bf16_output_rounding_is_exact(shape, sa, sb):
+    """One nonzero product per output (row code times column code, every E4M3 code on both
+    sides), so the float32 value before the bfloat16 store is known exactly: the stored bits
+    must be its round-to-nearest-even bfloat16, through ties, float32 and bfloat16 subnormals
+    (sb = 2^-120), overflow to infinity (sb = 2^110), signed zeros and NaN codes."""
+    M, N, K = shape
+    print(f"gemm bf16 rounding M={M} N={N} K={K} sa={sa} sb={sb}", flush=True)
+    A8 = np.zeros((M, K), np.uint8)
+    B8 = np.zeros((N, K), np.uint8)
+    A8[:, 0] = np.arange(M) % 256
+    B8[:, 0] = (np.arange(N) * 37 + 11) % 256
+    sa32, sb32 = np.float32(sa), np.float32(sb)
+    prod = np.outer(oracle.decode(A8[:, 0], F.E4M3), oracle.decode(B8[:, 0], F.E4M3))
+    with np.errstate(over="ignore", invalid="ignore"):
+        t = (prod * np.float64(sa32)).astype(np.float32)                  # acc * a_scale_inv
+        v = (t.astype(np.float64) * np.float64(sb32) + 0.0).astype(np.float32)   # * b_scale_inv + 0
+    want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    D = _run(A8, 0, float(sa32), B8, 0, float(sb32), None, 0)
+    got = D.cpu().view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(v)
+    assert nan.any() and np.isinf(v).any() == (sb > 1e30)
+    assert np.all((got[nan] & 0x7FFF) > 0x7F80), "NaN products must store a NaN"
+    assert np.array_equal(got[~nan], want[~nan])
