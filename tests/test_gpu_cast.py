@@ -158,7 +158,7 @@ def _dbias_bound(dyh):
     return 1e-5 * np.abs(S.bf16_bits_to_f64(dyh)).sum(axis=0) + 1e-30
 
 
-@pytest.mark.parametrize("shape", [(1, 1), (3, 5), (130, 264), (144, 264), (257, 383), (8192, 4096)])
+@pytest.mark.parametrize("shape", [(1, 1), (3, 5), (130, 264), (144, 264), (257, 383), (8192, 4096), (17297, 136)])
 def test_dbias_cast_transpose_parity(shape):
     print(f"dbias_cast_transpose {shape}", flush=True)
     R, C = shape
@@ -179,9 +179,12 @@ def test_dbias_cast_transpose_parity(shape):
     assert np.all(np.abs(got - rdb) <= _dbias_bound(dyh))
 
 
-def test_dbias_constant_columns_exact():
-    R, C = 8192, 64
-    dyh = np.full((R, C), 0x3F00, np.uint16)      # 0.5 everywhere: column sums 4096 exactly
+@pytest.mark.parametrize("R", [8192, 17297])
+def test_dbias_constant_columns_exact(R):
+    """0.5 everywhere: every partial and final sum is exact, so dbias = R / 2 exactly (136 row
+    tiles for R = 17297: whole 16-tile batches of the reduction plus single-tile remainders)."""
+    C = 64
+    dyh = np.full((R, C), 0x3F00, np.uint16)
     dy = bf16_dev(dyh)
     out = torch.empty((R, C), dtype=torch.uint8, device=DEV)
     out_t = torch.empty((C, R), dtype=torch.uint8, device=DEV)
@@ -189,7 +192,7 @@ def test_dbias_constant_columns_exact():
     ws = torch.empty(F.fp8_dbias_workspace_bytes(R, C), dtype=torch.uint8, device=DEV)
     F.fp8_dbias_cast_transpose(dy, scalar(1.0), F.E5M2, out, out_t, db, ws)
     torch.cuda.synchronize()
-    assert torch.all(db == 4096.0)
+    assert torch.all(db == R / 2)
 
 
 def test_dbias_deterministic():
