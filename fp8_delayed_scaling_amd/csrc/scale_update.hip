@@ -6,7 +6,9 @@
 //
 // One 256-thread block per tensor.  The history is [L][T] float32 (row 0 = current amaxes), so
 // a tensor's column is strided by T; at the sizes this runs at (L up to a few thousand, T up to
-// a few thousand) the kernel is launch-latency bound, not bandwidth bound.
+// a few thousand) the kernel is latency bound, not bandwidth bound.  A window of up to
+// kSuLdsRows rows is staged whole in LDS by direct loads (one memory round trip); the max and
+// the roll then read LDS.  Longer windows take the max and the roll in 256-row chunks.
 #include "device_common.h"
 #include "launch.h"
 
@@ -16,29 +18,55 @@ struct FmtMask {
     uint32_t bits[kMaxScaleTensors / 32];  // bit t set: tensor t is E5M2, else E4M3
 };
 
+constexpr int kSuLdsRows = 8192;
+
 __global__ __launch_bounds__(256) void k_scale_update(float *__restrict__ hist, int64_t L, int64_t T,
                                                       float *__restrict__ scale, float *__restrict__ scale_inv,
                                                       FmtMask fm, float pow2_neg_margin) {
     __shared__ float red[4];
     __shared__ int nanflag;
+    __shared__ __align__(16) float col[kSuLdsRows];
     const int64_t t = blockIdx.x;
     const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool staged = L <= kSuLdsRows;   // uniform
     if (tid == 0) nanflag = 0;
-    __syncthreads();
 
     // pass 1: max over the window (all L rows), NaN tracked on its own
-    float a = 0.f;
+    float a = 0.f, row0, prev_scale;
     bool nan = false;
-    for (int64_t i = tid; i < L; i += 256) {
-        const float h = hist[i * T + t];
-        nan |= (h != h);
-        a = fmaxf(a, h);
+    if (staged) {
+        // col[i] = hist[i][t] for every row: lane l of wave w loads row base + 64 w + l into that
+        // LDS slot (rows past the end re-read row L - 1; their slots, < 256 rounded-up rows, are
+        // never read).  No register depends on these loads, so all of them are in flight at once.
+        for (int64_t base = 0; base < L; base += 256) {
+            const int64_t i = min(base + tid, L - 1);
+            __builtin_amdgcn_global_load_lds((const void *)(hist + i * T + t),
+                                             (__attribute__((address_space(3))) void *)(col + base + wave * 64),
+                                             4, 0, 0);
+        }
+        prev_scale = scale[t];                // issued behind the history loads, overlapping them
+        __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0): this wave's rows have landed in LDS
+        __syncthreads();
+        for (int64_t i = tid; i < L; i += 256) {
+            const float h = col[i];
+            nan |= (h != h);
+            a = fmaxf(a, h);
+        }
+        row0 = col[0];
+    } else {
+        prev_scale = scale[t];
+        for (int64_t i = tid; i < L; i += 256) {
+            const float h = hist[i * T + t];
+            nan |= (h != h);
+            a = fmaxf(a, h);
+        }
+        row0 = hist[t];   // old row 0, read before any write below
     }
     if (nan) nanflag = 1;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
     if ((tid & 63) == 0) red[tid >> 6] = a;
-    const float row0 = hist[t];   // old row 0, read before any write below
     __syncthreads();
 
     if (tid == 0) {
@@ -49,19 +77,24 @@ __global__ __launch_bounds__(256) void k_scale_update(float *__restrict__ hist, 
         float s = (fmax / amax) * pow2_neg_margin;
         const bool bad = !(amax > 0.f) || !(amax < __uint_as_float(0x7F800000u)) ||
                          !(fabsf(s) < __uint_as_float(0x7F800000u)) || s == 0.f;
-        if (bad) s = scale[t];
+        if (bad) s = prev_scale;
         scale[t] = s;
         scale_inv[t] = 1.0f / s;
     }
 
-    // pass 2: roll towards row 0 in chunks of 256 rows (read row i+1, barrier, write row i)
-    for (int64_t base = 0; base < L - 1; base += 256) {
-        const int64_t i = base + tid;
-        float v = 0.f;
-        if (i < L - 1) v = hist[(i + 1) * T + t];
-        __syncthreads();
-        if (i < L - 1) hist[i * T + t] = v;
-        __syncthreads();
+    // pass 2: roll towards row 0 (new row i = old row i + 1 for i < L - 1)
+    if (staged) {
+        for (int64_t i = tid; i < L - 1; i += 256) hist[i * T + t] = col[i + 1];
+    } else {
+        // in chunks of 256 rows: read row i + 1, barrier, write row i
+        for (int64_t base = 0; base < L - 1; base += 256) {
+            const int64_t i = base + tid;
+            float v = 0.f;
+            if (i < L - 1) v = hist[(i + 1) * T + t];
+            __syncthreads();
+            if (i < L - 1) hist[i * T + t] = v;
+            __syncthreads();
+        }
     }
     if (tid == 0) {
         hist[(L - 1) * T + t] = row0;   // the amax just used becomes the newest past entry

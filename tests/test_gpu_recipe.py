@@ -45,8 +45,9 @@ def test_scale_update_backward_prep_config():
         assert _same(g, r)
 
 
-@pytest.mark.parametrize("L", [1, 2, 16, 257, 1024])
+@pytest.mark.parametrize("L", [1, 2, 16, 255, 256, 257, 1024, 8192, 8193, 9000])
 def test_scale_update_many_steps(L):
+    """Windows staged whole in LDS (L <= 8192) and longer ones rolled in chunks."""
     T = 5
     fm = [0, 1, 0, 1, 0]
     h = np.zeros((L, T), np.float32)
@@ -68,9 +69,8 @@ def test_scale_update_many_steps(L):
     assert _same(hd.cpu().numpy(), h) and _same(sd.cpu().numpy(), s) and _same(sid.cpu().numpy(), si)
 
 
-def test_scale_update_guard_cases_and_many_tensors():
-    T = 4096
-    L = 4
+@pytest.mark.parametrize("L,T", [(4, 4096), (9000, 64)])
+def test_scale_update_guard_cases_and_many_tensors(L, T):
     h = np.zeros((L, T), np.float32)
     h[:, :] = S.log_uniform_f32(91, L * T, 1e-6, 1e6).reshape(L, T)
     h[:, 0] = 0.0
