@@ -58,9 +58,9 @@ def parse():
 
 
 def traffic_probe():
-    """One plain copy of 1 GiB (known traffic: 1 GiB read + 1 GiB written) and one forward GEMM
-    launch at the QKV shape, nothing else on the GPU, so per-dispatch counters of the two can be
-    compared."""
+    """One plain copy of 1 GiB (known traffic: 1 GiB read + 1 GiB written), one forward GEMM
+    launch at the QKV shape, one cast+transpose of x [8192,12288] and one dbias+cast+transpose of
+    dy [8192,4096], nothing else on the GPU, so per-dispatch counters can be compared."""
     import torch
 
     import fp8_delayed_scaling_amd as F
@@ -80,7 +80,26 @@ def traffic_probe():
     torch.cuda.synchronize()
     F.fp8_gemm_bias(a8, F.E4M3, one, b8, F.E4M3, one, bias, y)
     torch.cuda.synchronize()
-    print(json.dumps({"traffic_probe": "done", "copy_bytes_each_way": 1 << 30, "gemm": [M, N, K]}))
+    del a8, b8, y
+    # inputs drawn on the device: no further copy dispatches beside the calibration copy
+    gd = torch.Generator(device=dev).manual_seed(12)
+    x = torch.randn((M, K), device=dev, generator=gd).to(torch.bfloat16)
+    x8, x8t = torch.empty((M, K), dtype=torch.uint8, device=dev), torch.empty((K, M), dtype=torch.uint8, device=dev)
+    sinv, am = torch.zeros(1, device=dev), torch.zeros(1, device=dev)
+    torch.cuda.synchronize()
+    F.fp8_cast_transpose(x, torch.full((1,), 0.4, device=dev), F.E4M3, x8, x8t, sinv, am)
+    torch.cuda.synchronize()
+    del x, x8, x8t
+    R, C = 8192, 4096
+    dy = (torch.randn((R, C), device=dev, generator=gd) * 0.01).to(torch.bfloat16)
+    d8, d8t = torch.empty((R, C), dtype=torch.uint8, device=dev), torch.empty((C, R), dtype=torch.uint8, device=dev)
+    db = torch.empty(C, device=dev)
+    ws = torch.empty(F.fp8_dbias_workspace_bytes(R, C), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    F.fp8_dbias_cast_transpose(dy, torch.full((1,), 4096.0, device=dev), F.E5M2, d8, d8t, db, ws, sinv, am)
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_probe": "done", "copy_bytes_each_way": 1 << 30, "gemm": [M, N, K],
+                      "cast_transpose": [M, K], "dbias_cast_transpose": [R, C]}))
 
 
 def log(*a):
