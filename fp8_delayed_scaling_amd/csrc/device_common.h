@@ -9,6 +9,8 @@ namespace fp8ds {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));        // one lane's 32 FP8 MFMA operand bytes
+typedef float f32x16 __attribute__((ext_vector_type(16)));    // one lane's 32 x 32 MFMA accumulators
 
 constexpr int kE4M3 = 0;
 constexpr int kE5M2 = 1;
@@ -116,6 +118,24 @@ __device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) 
         return pack4<FMT>(clamp_fmt<FMT>(a), clamp_fmt<FMT>(b), clamp_fmt<FMT>(c), clamp_fmt<FMT>(d));
     return encode_exact<FMT>(a) | (encode_exact<FMT>(b) << 8) | (encode_exact<FMT>(c) << 16) |
            (encode_exact<FMT>(d) << 24);
+}
+
+// float32 -> bfloat16, round to nearest even, by the hardware conversion (gfx950 converts two
+// values per instruction).  A NaN stays a NaN; its payload is not specified.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float lo, float hi) {
+    const bf16x2_t p = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+// GEMM epilogue arithmetic, acc * a_scale_inv * b_scale_inv + bias: one product, then one fused
+// multiply-add.  Every GEMM kernel and output dtype uses exactly this sequence, so they all see
+// the same float32 value.
+__device__ __forceinline__ float dequant_bias(float acc, float sa, float sb, float b) {
+    return __builtin_fmaf(acc * sa, sb, b);
 }
 
 }  // namespace fp8ds

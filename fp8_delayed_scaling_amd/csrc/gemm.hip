@@ -37,9 +37,6 @@
 
 namespace fp8ds {
 
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
 namespace {
 constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int kThreads = 256;
@@ -64,24 +61,7 @@ __device__ __forceinline__ void block_tile(int tiles_m, int tiles_n, int &tm, in
     tm = first_m + in_group % gm;
     tn = in_group / gm;
 }
-
-// float32 -> bfloat16, round to nearest even, by the hardware conversion (gfx950 converts two
-// values per instruction).  A NaN stays a NaN; its payload is not specified.
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
-    return __builtin_bit_cast(uint16_t, (__bf16)v);
-}
-__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float lo, float hi) {
-    const bf16x2_t p = {(__bf16)lo, (__bf16)hi};
-    return __builtin_bit_cast(uint32_t, p);
-}
 }  // namespace
-
-// acc * a_scale_inv * b_scale_inv + bias: one product, then one fused multiply-add.  Every
-// epilogue uses exactly this sequence, so all output dtypes see the same float32 value.
-__device__ __forceinline__ float dequant_bias(float acc, float sa, float sb, float b) {
-    return __builtin_fmaf(acc * sa, sb, b);
-}
 
 // FP8 output (OUT 2 = E4M3, 3 = E5M2): D is encoded with its own scale, max |D| (float32, before
 // the scale) is folded into an amax slot, and block 0 records 1/scale as the output's private
@@ -661,11 +641,16 @@ __global__ __launch_bounds__(64) void k_gemm_small(const uint8_t *__restrict__ A
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     // the inverse scales, output scale and bias are read before the K loop, so their latency
-    // overlaps the operand loads; bias columns past N read bias[N - 1] (never stored)
+    // overlaps the operand loads; bias columns past N read bias[N - 1] (never stored).  The bias
+    // loads are unconditional (without a bias they read the first two bytes of a_sinv) and the
+    // raw bits are kept: a load inside a branch, or a select right after it, would wait for each
+    // load in turn; the bias itself is chosen where it is used.
     const float sa = *a_sinv, sb = *b_sinv;
     float ds = 0.f;
     if constexpr (OUT >= 2) ds = *oq.scale;
-    float bv[2][4][4];
+    const bool has_bias = bias != nullptr;
+    const uint16_t *bsrc = has_bias ? bias : reinterpret_cast<const uint16_t *>(a_sinv);
+    uint32_t braw[2][4][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -673,7 +658,7 @@ __global__ __launch_bounds__(64) void k_gemm_small(const uint8_t *__restrict__ A
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int col = min(n0 + j * 32 + q * 8 + fhalf * 4 + u, N - 1);
-                bv[j][q][u] = bias != nullptr ? __uint_as_float((uint32_t)bias[col] << 16) : 0.f;
+                braw[j][q][u] = bsrc[has_bias ? col : 0];
             }
     const int nk = K / kPK;
 #define FP8DS_SLOAD(FA_, FB_, kt)                                                                          \
@@ -718,7 +703,8 @@ __global__ __launch_bounds__(64) void k_gemm_small(const uint8_t *__restrict__ A
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int col = n0 + j * 32 + (e >> 2) * 8 + fhalf * 4 + (e & 3);
-                const float v = dequant_bias(acc[i][j][e], sa, sb, bv[j][e >> 2][e & 3]);
+                const float b = has_bias ? __uint_as_float(braw[j][e >> 2][e & 3] << 16) : 0.f;
+                const float v = dequant_bias(acc[i][j][e], sa, sb, b);
                 if (row < M && col < N) {
                     const int64_t o = (int64_t)row * ldd + col;
                     if constexpr (OUT == 0) {
