@@ -9,6 +9,7 @@ namespace fp8ds {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));   // two 16-bit values in one register
 typedef int i32x8 __attribute__((ext_vector_type(8)));        // one lane's 32 FP8 MFMA operand bytes
 typedef float f32x16 __attribute__((ext_vector_type(16)));    // one lane's 32 x 32 MFMA accumulators
 

@@ -84,11 +84,18 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], const float 
     float ds = 0.f;
     if constexpr (OUT >= 2) ds = *oq.scale;
     uint32_t amag = 0;
+    // the four bias columns, loaded together (unconditional loads: without a bias they read the
+    // first two bytes of a_sinv) before any is used
+    const bool has_bias = bias != nullptr;
+    const uint16_t *bsrc = has_bias ? bias : reinterpret_cast<const uint16_t *>(a_sinv);
+    uint32_t braw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) braw[j] = bsrc[has_bias ? min(col0 + j * 32 + frow, N - 1) : 0];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int col = col0 + j * 32 + frow;
         if (col >= N) continue;
-        const float bv = bias != nullptr ? __uint_as_float((uint32_t)bias[col] << 16) : 0.f;
+        const float bv = has_bias ? __uint_as_float(braw[j] << 16) : 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -125,25 +132,24 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], const float 
 // ragged right edge, the elements are stored one by one.
 template <int OUT>
 __device__ __forceinline__ void epilogue_staged(const f32x16 (&acc)[4][4], float sa, float sb, float ds,
-                                                const uint16_t *__restrict__ bias, void *__restrict__ D, int64_t ldd,
-                                                int M, int N, int row0, int col0, int lane, uint8_t *wlds,
-                                                OutQuant oq) {
+                                                bool has_bias, const us2 (&braw)[4][4][2],
+                                                void *__restrict__ D, int64_t ldd, int M, int N, int row0,
+                                                int col0, int lane, uint8_t *wlds, OutQuant oq) {
     const int frow = lane & 31, fhalf = lane >> 5;
     constexpr int kElemsPer16 = OUT == 0 ? 8 : OUT == 1 ? 4 : 16;
     const bool vec_ok = ((reinterpret_cast<uintptr_t>(D) & 15u) == 0) && (ldd % kElemsPer16 == 0);
-    // bias of the 16 columns this lane holds in column block j.  Columns past N read bias[N - 1]:
-    // their operand rows are clamped to row N - 1 of B, so every value a lane holds outside the
-    // output (rows past M read row M - 1 of A) is bit-identical to an element inside it.  Such
-    // values are never stored, and the FP8 output's amax can take the max over the whole
-    // sub-tile without masking.
+    // bias of the 16 columns this lane holds in column block j, from the raw bits the caller
+    // loaded (braw[j][q][u / 2][u % 2] = bias[min(col0 + 32 j + 8 q + 4 (lane / 32) + u, N - 1)]).
+    // Columns past N take bias[N - 1]: their operand rows are clamped to row N - 1 of B, so every
+    // value a lane holds outside the output (rows past M read row M - 1 of A) is bit-identical to
+    // an element inside it.  Such values are never stored, and the FP8 output's amax can take the
+    // max over the whole sub-tile without masking.
     auto load_bias = [&](int j, float (&bv)[4][4]) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int col = min(col0 + j * 32 + q * 8 + fhalf * 4 + u, N - 1);
-                bv[q][u] = bias != nullptr ? __uint_as_float((uint32_t)bias[col] << 16) : 0.f;
-            }
+            for (int u = 0; u < 4; ++u)
+                bv[q][u] = has_bias ? __uint_as_float((uint32_t)braw[j][q][u >> 1][u & 1] << 16) : 0.f;
     };
     if constexpr (OUT == 0) {
 #pragma unroll
@@ -566,30 +572,53 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias_pipe(const uint8_t *_
         FP8DS_STEP(kt + 2, st3, st1, fa0, fb0, fa1, fb1)
         FP8DS_STEP(kt + 3, st0, st2, fa1, fb1, fa0, fb0)
     }
-    // remaining slices (fewer than 7): everything in flight is waited for, fragments re-read
-    for (; kt < nk; ++kt) {
-        FP8DS_WAIT_VM(0);
-        FP8DS_BARRIER();
-        if (kt + 3 < nk) {
-            const int s3 = (kt + 3) & 3;
-            if (s3 == 0) { FP8DS_ISSUE(st0, kt + 3) }
-            else if (s3 == 1) { FP8DS_ISSUE(st1, kt + 3) }
-            else if (s3 == 2) { FP8DS_ISSUE(st2, kt + 3) }
-            else { FP8DS_ISSUE(st3, kt + 3) }
-        }
-        const int sc = kt & 3;
-        const uint8_t *cur = sc == 0 ? st0 : sc == 1 ? st1 : sc == 2 ? st2 : st3;
-        i32x8 ta[4], tb[4];
-        FP8DS_FRAGS(cur, ta, tb)
-        FP8DS_MFMA(ta, tb)
+    // The last slices (fewer than 7; the steady loop leaves kt % 4 == 0, so the stages keep the
+    // same rotation): the steady step without the issues that would pass the end of K, waiting
+    // only for the next slice (8 loads, of the slice after it, may stay in flight); the last
+    // slice needs no wait, fragments or barrier.  Every condition is uniform across the block.
+#define FP8DS_TSTEP(kt, NXT1, ISS, CA, CB, NA, NB)                                                        \
+    if ((kt) < nk) {                                                                                      \
+        if ((kt) + 1 < nk) {                                                                              \
+            __builtin_amdgcn_sched_barrier(0);                                                            \
+            if ((kt) + 2 < nk) FP8DS_WAIT_VM(8);                                                          \
+            else FP8DS_WAIT_VM(0);                                                                        \
+            FP8DS_BARRIER();                                                                              \
+            __builtin_amdgcn_sched_barrier(0);                                                            \
+            if ((kt) + 3 < nk) { FP8DS_ISSUE(ISS, (kt) + 3) }                                             \
+            FP8DS_FRAGS(NXT1, NA, NB)                                                                     \
+        }                                                                                                 \
+        FP8DS_MFMA(CA, CB)                                                                                \
+        __builtin_amdgcn_sched_barrier(0);                                                                \
     }
+    FP8DS_TSTEP(kt + 0, st1, st3, fa0, fb0, fa1, fb1)
+    FP8DS_TSTEP(kt + 1, st2, st0, fa1, fb1, fa0, fb0)
+    FP8DS_TSTEP(kt + 2, st3, st1, fa0, fb0, fa1, fb1)
+    FP8DS_TSTEP(kt + 3, st0, st2, fa1, fb1, fa0, fb0)
+    FP8DS_TSTEP(kt + 4, st1, st3, fa0, fb0, fa1, fb1)
+    FP8DS_TSTEP(kt + 5, st2, st0, fa1, fb1, fa0, fb0)
+#undef FP8DS_TSTEP
 #undef FP8DS_ISSUE
 #undef FP8DS_FRAGS
 #undef FP8DS_MFMA
 #undef FP8DS_STEP
     __syncthreads();   // every wave is done reading the operand stages
     uint8_t *wl = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
-    epilogue_staged<OUT>(acc, sa, sb, ds, bias, D, ldd, M, N, m0 + wm * 128, n0 + wn * 128, lane, wl, oq);
+    // The bias of the 64 columns this lane holds, two values per register, loaded together before
+    // the epilogue uses them: a load guarded by the null check (or a select right after it) would
+    // be waited for on its own, one memory round trip per column.  Without a bias the loads read
+    // the first two bytes of a_sinv.
+    const bool has_bias = bias != nullptr;
+    const uint16_t *bsrc = has_bias ? bias : reinterpret_cast<const uint16_t *>(a_sinv);
+    const int col0 = n0 + wn * 128, bhalf = lane >> 5;
+    us2 braw[4][4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                braw[j][q][u >> 1][u & 1] = bsrc[has_bias ? min(col0 + j * 32 + q * 8 + bhalf * 4 + u, N - 1) : 0];
+    epilogue_staged<OUT>(acc, sa, sb, ds, has_bias, braw, D, ldd, M, N, m0 + wm * 128, col0, lane, wl, oq);
 }
 
 // ------------------------------------------------------------------------------------------
