@@ -54,7 +54,42 @@ def parse():
     p.add_argument("--traffic-probe", action="store_true",
                    help="only launch one plain 1 GiB device copy and one forward GEMM (for rocprofv3 --pmc "
                         "FETCH_SIZE / WRITE_SIZE passes: the copy calibrates the counters)")
+    p.add_argument("--mfma-probe", action="store_true",
+                   help="only launch the forward GEMM three times and the vendor library's FP8 GEMM "
+                        "(torch._scaled_mm) three times on the same operands (for rocprofv3 --pmc passes "
+                        "comparing matrix-core busy cycles, wait cycles and total cycles)")
     return p.parse_args()
+
+
+def mfma_probe():
+    """The forward QKV GEMM of this library and torch._scaled_mm (hipBLASLt) on the same FP8
+    operands -- x ~ N(0,1) and W ~ N(0,0.02) cast to E4M3 by this library's cast -- three launches
+    each, synchronised one by one, nothing else on the GPU."""
+    import torch
+
+    import fp8_delayed_scaling_amd as F
+
+    F.lib()
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(13)
+    x = torch.randn((M, K), device=dev, generator=g).to(torch.bfloat16)
+    w = (torch.randn((N, K), device=dev, generator=g) * 0.02).to(torch.bfloat16)
+    x8, w8 = torch.empty((M, K), dtype=torch.uint8, device=dev), torch.empty((N, K), dtype=torch.uint8, device=dev)
+    sx, sw = torch.full((1,), 60.0, device=dev), torch.full((1,), 2000.0, device=dev)
+    six, siw = torch.zeros(1, device=dev), torch.zeros(1, device=dev)
+    F.fp8_cast_amax(x, sx, F.E4M3, x8.view(-1), six, None)
+    F.fp8_cast_amax(w, sw, F.E4M3, w8.view(-1), siw, None)
+    del x, w
+    y = torch.empty((M, N), device=dev, dtype=torch.bfloat16)
+    a8, b8 = x8.view(torch.float8_e4m3fn), w8.view(torch.float8_e4m3fn)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        F.fp8_gemm_bias(x8, F.E4M3, six, w8, F.E4M3, siw, None, y)
+        torch.cuda.synchronize()
+    for _ in range(3):
+        torch._scaled_mm(a8, b8.t(), scale_a=six[0], scale_b=siw[0], out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+    print(json.dumps({"mfma_probe": "done", "gemm": [M, N, K]}))
 
 
 def traffic_probe():
@@ -110,6 +145,9 @@ def main():
     args = parse()
     if args.traffic_probe:
         traffic_probe()
+        return
+    if args.mfma_probe:
+        mfma_probe()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; sharding across GPUs is described, "
