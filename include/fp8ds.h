@@ -231,12 +231,15 @@ int fp8_transpose(const uint8_t *in, int64_t rows, int64_t cols, uint8_t *out_t,
 /*
  * fp8_linear_fwd -- forward of the FP8 linear layer y = x W^T + bias ([WS] description: one
  * FP8 weight workspace with its transpose; [CG] feature list: FP8 weight caching).
- * Launch sequence on `stream`:
+ * Work enqueued on `stream`, in this order:
  *   1. x8 = cast(x, *x_scale) E4M3 (cast+transpose when x8_t != NULL, else cast only),
  *      amax into *x_amax, *x_scale_inv = 1/(*x_scale);
  *   2. w8, w8_t = cast_transpose(W, *w_scale) E4M3, amax into *w_amax, *w_scale_inv written;
  *      skipped on the device when w_noop != NULL and *w_noop == 1.0f (cached weight);
  *   3. y = gemm_bias(x8, w8) with *x_scale_inv, *w_scale_inv and bias.
+ * Steps 1 and 2 are one kernel launch when both tensors take the same cast code path (M and N
+ * both multiples of 16 with K a multiple of 8, or neither), else two; the results are those of
+ * the separate calls either way.
  * x: [M, K], W: [N, K], bias: [N] or NULL (bfloat16).  x8: [M, K], x8_t: [K, M] or NULL,
  * w8: [N, K], w8_t: [K, N] codes.  y: [M, N] bfloat16.  K % 16 == 0.
  */
