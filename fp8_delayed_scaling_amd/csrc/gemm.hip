@@ -699,21 +699,24 @@ __global__ __launch_bounds__(64) void k_gemm_small(const uint8_t *__restrict__ A
     _Pragma("unroll") for (int i = 0; i < 2; ++i)                                                         \
     _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                         \
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(FB_[j], FA_[i], acc[i][j], FB, FA, 0, 0, 0, 0);
+    // The loads are unconditional (slice indices clamped to the last slice; the extra loads at
+    // the end stay in bounds and are never used): a load behind a branch leaves the compiler
+    // unable to count what is in flight, and it then waits for every outstanding load.
     i32x8 a0[2], b0[2], a1[2], b1[2], a2[2], b2[2], a3[2], b3[2];
     FP8DS_SLOAD(a0, b0, 0)
-    if (nk > 1) { FP8DS_SLOAD(a1, b1, 1) }
-    if (nk > 2) { FP8DS_SLOAD(a2, b2, 2) }
-    if (nk > 3) { FP8DS_SLOAD(a3, b3, 3) }
+    FP8DS_SLOAD(a1, b1, min(1, nk - 1))
+    FP8DS_SLOAD(a2, b2, min(2, nk - 1))
+    FP8DS_SLOAD(a3, b3, min(3, nk - 1))
     int kt = 0;
     for (; kt + 4 <= nk; kt += 4) {
         FP8DS_SMFMA(a0, b0)
-        if (kt + 4 < nk) { FP8DS_SLOAD(a0, b0, kt + 4) }
+        FP8DS_SLOAD(a0, b0, min(kt + 4, nk - 1))
         FP8DS_SMFMA(a1, b1)
-        if (kt + 5 < nk) { FP8DS_SLOAD(a1, b1, kt + 5) }
+        FP8DS_SLOAD(a1, b1, min(kt + 5, nk - 1))
         FP8DS_SMFMA(a2, b2)
-        if (kt + 6 < nk) { FP8DS_SLOAD(a2, b2, kt + 6) }
+        FP8DS_SLOAD(a2, b2, min(kt + 6, nk - 1))
         FP8DS_SMFMA(a3, b3)
-        if (kt + 7 < nk) { FP8DS_SLOAD(a3, b3, kt + 7) }
+        FP8DS_SLOAD(a3, b3, min(kt + 7, nk - 1))
     }
     // the last nk % 4 slices, already in a0, a1, a2 in K order
     if (kt < nk) { FP8DS_SMFMA(a0, b0) }
