@@ -17,9 +17,10 @@
 // stores.  No split-K: every output element is one fixed sequence of MFMAs over K in the same
 // K order in both kernels, whatever tile it falls in.
 //
-// k_gemm_bias_pipe (K % 64 == 0, the hot path): a 4-stage pipeline of 64-byte K slices
-// (4 x 32 KB of LDS).  Global memory goes straight into LDS with global_load_lds_dwordx4 (no
-// staging registers), three slices ahead of the MFMAs; each wave prefetches the next slice's
+// k_gemm_bias_pipe (K % 64 == 0 and row strides below 8 MiB, the hot path): a 4-stage pipeline
+// of 64-byte K slices (4 x 32 KB of LDS).  Global memory goes straight into LDS with
+// buffer_load_dwordx4 ... lds (no staging registers; per-tile descriptors, 32-bit per-lane
+// offsets, the K slice in the scalar offset), three slices ahead of the MFMAs; each wave prefetches the next slice's
 // operand fragments from LDS while its MFMAs run on the current ones (double-buffered
 // fragments), and the instruction scheduler is told to interleave one MFMA with one LDS read and
 // every other MFMA with one global load.  The four stages are four distinct LDS arrays so the
@@ -438,6 +439,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias(const uint8_t *__rest
 // ------------------------------------------------------------------------------------------
 namespace {
 constexpr int kPK = 64;                          // K bytes per pipeline slice
+// Word 3 of a raw buffer descriptor (no format conversion, bounds checked against the byte
+// count in word 2).
+constexpr int kBufDesc3 = 0x00020000;
+// Row strides below this keep a 256-row tile's extent, the buffer bound, under 2^31 bytes.
+constexpr int64_t kPipeMaxLd = INT64_C(1) << 23;
 constexpr int kPStage = (BM + BN) * kPK;         // 32 KB: A rows then B rows, 64 bytes each
 __device__ __forceinline__ int pswz(int r) { return (r >> 2) & 3; }
 }  // namespace
@@ -483,22 +489,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias_pipe(const uint8_t *_
     // Direct loads: a slice is 2048 chunks of 16 bytes; load i of wave w writes the 1 KB of the
     // stage at (i * 4 + w) * 1024, lane l at + 16 l.  Position p holds row p / 64 (A rows 0-255,
     // then B rows) and stored chunk (p / 16) % 4, i.e. source chunk stored ^ pswz(row).
-    const uint8_t *src[8];
+    // The loads are buffer loads into LDS: one descriptor per operand whose base is the tile's
+    // first row and whose bound is the tile's extent (256 rows x lda bytes, below 2^31 as the
+    // launcher requires), a 32-bit offset per lane and the K slice in the scalar offset.  Against
+    // 64-bit per-lane addresses this saves the per-slice address arithmetic and lets the compiler
+    // count the LDS reads in flight exactly; an offset past the bound would read zeros.
+    const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
+    const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(A + (int64_t)m0 * lda), (short)0, (int)(rows_a * lda), kBufDesc3);
+    const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(B + (int64_t)n0 * ldb), (short)0, (int)(rows_b * ldb), kBufDesc3);
+    uint32_t voff[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int p = (i * 4 + wave) * 1024 + lane * 16;
         const int row = p >> 6, slot = (p >> 4) & 3;
         const int r = row & 255;
         const int c = slot ^ pswz(r);
-        src[i] = row < 256 ? A + (int64_t)min(m0 + r, M - 1) * lda + c * 16
-                           : B + (int64_t)min(n0 + r, N - 1) * ldb + c * 16;
+        voff[i] = row < 256 ? (uint32_t)(min(r, rows_a - 1) * lda + c * 16)
+                            : (uint32_t)(min(r, rows_b - 1) * ldb + c * 16);
     }
     const int nk = K / kPK;
 #define FP8DS_ISSUE(ST, kt)                                                                               \
     _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                         \
-        __builtin_amdgcn_global_load_lds((const void *)(src[i] + (int64_t)(kt) * kPK),                    \
-                                         (__attribute__((address_space(3))) void *)((ST) + (i * 4 + wave) * 1024), \
-                                         16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(i < 4 ? rs_a : rs_b,                                      \
+                                                 (__attribute__((address_space(3))) void *)((ST) + (i * 4 + wave) * 1024), \
+                                                 16, voff[i], (uint32_t)((kt) * kPK), 0, 0);
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -809,8 +825,9 @@ hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64
     }
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
     dim3 grid((unsigned)(tiles_m * tiles_n));
-    const bool pipe = (K % kPK) == 0;
-    const bool small = pipe && (int64_t)tiles_m * tiles_n < kSmallTiles;
+    const bool k64 = (K % kPK) == 0;
+    const bool pipe = k64 && lda < kPipeMaxLd && ldb < kPipeMaxLd;
+    const bool small = k64 && (int64_t)tiles_m * tiles_n < kSmallTiles;
     const int stiles_n = (int)((N + kSmallTile - 1) / kSmallTile);
     dim3 sgrid((unsigned)(((M + kSmallTile - 1) / kSmallTile) * stiles_n));
 #define FP8DS_GEMM(FA_, FB_, O_)                                                                           \
