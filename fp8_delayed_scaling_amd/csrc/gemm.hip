@@ -22,8 +22,8 @@
 // buffer_load_dwordx4 ... lds (no staging registers; per-tile descriptors, 32-bit per-lane
 // offsets, the K slice in the scalar offset), three slices ahead of the MFMAs; each wave prefetches the next slice's
 // operand fragments from LDS while its MFMAs run on the current ones (double-buffered
-// fragments), and the instruction scheduler is told to interleave one MFMA with one LDS read and
-// every other MFMA with one global load.  The four stages are four distinct LDS arrays so the
+// fragments), and the instruction scheduler is told to place the fragment reads and global loads
+// among the first 12 of the slice's 16 MFMAs.  The four stages are four distinct LDS arrays so the
 // compiler can tell the in-flight loads of one stage from the reads of another, and the
 // per-slice barrier is a bare s_barrier after an explicit vmcnt wait (a fenced barrier would
 // drain every load in flight).  LDS rows are 64 bytes; 16-byte chunk c of row r sits at chunk
@@ -554,7 +554,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias_pipe(const uint8_t *_
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                         \
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(CB[j], CA[i], acc[i][j], FB, FA, 0, 0, 0, 0);
     // One slice: wait for slice kt+1, barrier, issue slice kt+3 into the stage slice kt-1 used,
-    // prefetch slice kt+1's fragments, run slice kt's 16 MFMAs (interleaved by the scheduler).
+    // prefetch slice kt+1's fragments, run slice kt's 16 MFMAs.  The scheduler places the 16
+    // fragment reads and the 8 loads among the first 12 MFMAs (per three MFMAs: four reads, two
+    // loads) and leaves the last four MFMAs free, so the reads have landed before the next
+    // slice's wait (3% faster on the three QKV GEMM shapes than one read per MFMA throughout).
 #define FP8DS_STEP(kt, NXT1, ISS, CA, CB, NA, NB)                                                         \
     __builtin_amdgcn_sched_barrier(0);                                                                    \
     FP8DS_WAIT_VM(8);                                                                                     \
@@ -563,11 +566,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias_pipe(const uint8_t *_
     FP8DS_ISSUE(ISS, (kt) + 3)                                                                            \
     FP8DS_FRAGS(NXT1, NA, NB)                                                                             \
     FP8DS_MFMA(CA, CB)                                                                                    \
-    _Pragma("unroll") for (int q = 0; q < 16; ++q) {                                                      \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                                       \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                \
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                                \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                \
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                \
-        if (q & 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                     \
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                                \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                \
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                                \
     }                                                                                                     \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      \
     __builtin_amdgcn_sched_barrier(0);
 
     i32x8 fa0[4], fb0[4], fa1[4], fb1[4];
