@@ -287,7 +287,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "k_gemm_bias (fwd/dgrad/wgrad average)",
+            "kernel": "k_gemm_pipe16 (fwd/dgrad/wgrad average)",
             "achieved": round(gemm_tflops, 2),
             "peak": FP8_PEAK / 1e12,
             "unit": "TFLOP/s",

@@ -12,6 +12,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));   // two 16-bit values in one register
 typedef int i32x8 __attribute__((ext_vector_type(8)));        // one lane's 32 FP8 MFMA operand bytes
 typedef float f32x16 __attribute__((ext_vector_type(16)));    // one lane's 32 x 32 MFMA accumulators
+typedef float f32x4 __attribute__((ext_vector_type(4)));      // one lane's 16 x 16 MFMA accumulators
 
 constexpr int kE4M3 = 0;
 constexpr int kE5M2 = 1;

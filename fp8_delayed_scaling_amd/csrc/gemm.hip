@@ -7,27 +7,38 @@
 // fix).  Both operands are K-contiguous ("TN"); the transposes the backward needs come from
 // the cast+transpose kernels, so the GEMM never transposes.
 //
-// Both kernels: block tile 256 x 256, 256 threads = 4 waves in a 2 x 2 grid, each wave a 128 x 128
-// sub-tile made of 4 x 4 v_mfma_f32_32x32x64_f8f6f4 tiles (float32 accumulate; the A / B formats
-// are the instruction's cbsz / blgp selectors, so every format pair shares one template).
-// Blocks are remapped so that each XCD (blocks are dealt round-robin to the 8 XCDs) works on a
-// contiguous range of tiles, walked in groups of kGroupM tile-rows for L2 reuse.  Epilogue:
-// acc * a_scale_inv * b_scale_inv + bias in float32, rounded to bfloat16 (nearest even) or stored
-// as float32 (the pipelined kernel stages it through LDS and writes 16-byte row segments).  Ragged M / N are handled by clamping the rows that are loaded and masking the
-// stores.  No split-K: every output element is one fixed sequence of MFMAs over K in the same
-// K order in both kernels, whatever tile it falls in.
+// Two kernel families, chosen from K and the row strides alone (never from M or N, so every
+// N-chunk of a GEMM takes the same family as the whole):
+//   * the 16 x 16 x 128 family (K % 256 == 0, row strides below 8 MiB; the hot path):
+//     k_gemm_pipe16 (256 x 256 tiles, 2 x 2 waves of 128 x 128 made of 8 x 8
+//     v_mfma_f32_16x16x128_f8f6f4 tiles) and k_gemm_small16 (one wave per 64 x 64 tile, for
+//     problems under 40 large tiles);
+//   * the 32 x 32 x 64 family (every other K % 16 == 0): k_gemm_bias_pipe (K % 64 == 0, strides
+//     below 8 MiB), k_gemm_small (K % 64 == 0, under 40 large tiles) and k_gemm_bias (general
+//     K, tail zero-filled), waves of 4 x 4 v_mfma_f32_32x32x64_f8f6f4 tiles.
+// Inside a family every output element is one fixed sequence of MFMAs over K in the same K
+// order, whatever kernel or tile it falls in, so the kernels of a family give identical bits
+// (no split-K).  The two families differ in the last bits now and then: the 16 x 16 x 128 MFMA
+// sums 128 products per instruction, the 32 x 32 x 64 one 64.  Float32 accumulate; the A / B
+// formats are the instruction's cbsz / blgp selectors, so every format pair shares one template.
+// Blocks of the 256 x 256 kernels are remapped so that each XCD (blocks are dealt round-robin to
+// the 8 XCDs) works on a contiguous range of tiles, walked in groups of kGroupM tile-rows for L2
+// reuse.  Epilogue: acc * a_scale_inv * b_scale_inv + bias in float32, rounded to bfloat16
+// (nearest even), stored as float32, or encoded to FP8 with amax capture (the pipelined kernels
+// stage it through LDS and write 16-byte row segments).  Ragged M / N are handled by clamping the
+// rows that are loaded and masking the stores.
 //
-// k_gemm_bias_pipe (K % 64 == 0 and row strides below 8 MiB, the hot path): a 4-stage pipeline
-// of 64-byte K slices (4 x 32 KB of LDS).  Global memory goes straight into LDS with
-// buffer_load_dwordx4 ... lds (no staging registers; per-tile descriptors, 32-bit per-lane
-// offsets, the K slice in the scalar offset), three slices ahead of the MFMAs; each wave prefetches the next slice's
-// operand fragments from LDS while its MFMAs run on the current ones (double-buffered
-// fragments), and the instruction scheduler is told to place the fragment reads and global loads
-// among the first 12 of the slice's 16 MFMAs.  The four stages are four distinct LDS arrays so the
-// compiler can tell the in-flight loads of one stage from the reads of another, and the
-// per-slice barrier is a bare s_barrier after an explicit vmcnt wait (a fenced barrier would
-// drain every load in flight).  LDS rows are 64 bytes; 16-byte chunk c of row r sits at chunk
-// c ^ ((r >> 2) & 3), which measured bank-conflict free for the MFMA operand reads.
+// k_gemm_bias_pipe: a 4-stage pipeline of 64-byte K slices (4 x 32 KB of LDS).  Global memory goes
+// straight into LDS with buffer_load_dwordx4 ... lds (no staging registers; per-tile descriptors,
+// 32-bit per-lane offsets, the K slice in the scalar offset), three slices ahead of the MFMAs;
+// each wave prefetches the next slice's operand fragments from LDS while its MFMAs run on the
+// current ones (double-buffered fragments), and the instruction scheduler is told to place the
+// fragment reads and global loads among the first 12 of the slice's 16 MFMAs.  The four stages
+// are four distinct LDS arrays so the compiler can tell the in-flight loads of one stage from the
+// reads of another, and the per-slice barrier is a bare s_barrier after an explicit vmcnt wait (a
+// fenced barrier would drain every load in flight).  LDS rows are 64 bytes; 16-byte chunk c of
+// row r sits at chunk c ^ ((r >> 2) & 3), which measured bank-conflict free for the MFMA operand
+// reads.  k_gemm_pipe16 (further down) keeps these techniques with 128-byte K steps.
 //
 // k_gemm_bias (any K % 16 == 0): global -> registers -> LDS with double-buffered 128-byte K
 // slices, the K tail zero-filled.
@@ -123,52 +134,89 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[4][4], const float 
     }
 }
 
-// Epilogue of the pipelined kernel, whose MFMAs take B as the first operand: there lane l holds
-// D[row0 + 32 i + l % 32][col0 + 32 j + 8 (e / 4) + 4 (l / 32) + e % 4] in element e of acc[i][j]
-// (the products and their summation order are the same as with A first).  Each wave scales, adds
-// the bias and rounds its 128 x 128 sub-tile into its own 32 KB of LDS, then writes whole rows
-// with 16-byte streaming (nontemporal) stores.  bf16: one pass, row r at r * 256, 8-byte slot s
-// (columns 4 s .. 4 s + 3) stored at slot s ^ (r & 31).  float32: two passes of 64 rows, row r at
-// r * 512, 16-byte slot s at s ^ (r & 31).  Where D or ldd is not 16-byte aligned, or at the
-// ragged right edge, the elements are stored one by one.
-template <int OUT>
-__device__ __forceinline__ void epilogue_staged(const f32x16 (&acc)[4][4], float sa, float sb, float ds,
-                                                bool has_bias, const us2 (&braw)[4][4][2],
-                                                void *__restrict__ D, int64_t ldd, int M, int N, int row0,
-                                                int col0, int lane, uint8_t *wlds, OutQuant oq) {
-    const int frow = lane & 31, fhalf = lane >> 5;
-    constexpr int kElemsPer16 = OUT == 0 ? 8 : OUT == 1 ? 4 : 16;
-    const bool vec_ok = ((reinterpret_cast<uintptr_t>(D) & 15u) == 0) && (ldd % kElemsPer16 == 0);
-    // bias of the 16 columns this lane holds in column block j, from the raw bits the caller
-    // loaded (braw[j][q][u / 2][u % 2] = bias[min(col0 + 32 j + 8 q + 4 (lane / 32) + u, N - 1)]).
-    // Columns past N take bias[N - 1]: their operand rows are clamped to row N - 1 of B, so every
-    // value a lane holds outside the output (rows past M read row M - 1 of A) is bit-identical to
-    // an element inside it.  Such values are never stored, and the FP8 output's amax can take the
-    // max over the whole sub-tile without masking.
-    auto load_bias = [&](int j, float (&bv)[4][4]) {
+// A wave's 128 x 128 accumulator sub-tile seen as 64 "quads" of four consecutive columns of one
+// row, in one of the two MFMA layouts the pipelined kernels use (both take B as the MFMA's first
+// operand; the products and their summation order are the same as with A first).  visit<RLO, RHI>
+// calls f(r, sl, v) for every quad whose sub-tile row r lies in [RLO, RHI), with sl the 4-column
+// slot (columns 4 sl .. 4 sl + 3) and v the four values after acc * a_scale_inv * b_scale_inv +
+// bias.  The bias comes from raw bits the kernel loaded before its epilogue; columns past N take
+// bias[N - 1]: their operand rows are clamped to row N - 1 of B, so every value a lane holds
+// outside the output (rows past M read row M - 1 of A) is bit-identical to an element inside it.
+// Such values are never stored, and the FP8 output's amax can take the max over the whole
+// sub-tile without masking.
+//
+// 32 x 32 x 64 MFMAs: lane l holds D[row0 + 32 i + l % 32][col0 + 32 j + 8 q + 4 (l / 32) + u] in
+// element 4 q + u of acc[i][j]; braw[j][q][u / 2][u % 2] = bias[col0 + 32 j + 8 q + 4 (l / 32) + u].
+struct Quads32 {
+    const f32x16 (&acc)[4][4];
+    const us2 (&braw)[4][4][2];
+    bool has_bias;
+    float sa, sb;
+    int lane;
+    template <int RLO, int RHI, class F>
+    __device__ __forceinline__ void visit(F &&f) const {
+        const int frow = lane & 31, fhalf = lane >> 5;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                bv[q][u] = has_bias ? __uint_as_float((uint32_t)braw[j][q][u >> 1][u & 1] << 16) : 0.f;
-    };
-    if constexpr (OUT == 0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float bv[4][4];
-            load_bias(j, bv);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i) {
+                if (i * 32 < RLO || i * 32 >= RHI) continue;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int r = i * 32 + frow, sl = j * 8 + q * 2 + fhalf;
                     float v[4];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) v[u] = dequant_bias(acc[i][j][q * 4 + u], sa, sb, bv[q][u]);
-                    const u32x2 pk = {f32x2_to_bf16x2_rne(v[0], v[1]), f32x2_to_bf16x2_rne(v[2], v[3])};
-                    *reinterpret_cast<u32x2 *>(wlds + r * 256 + ((sl ^ (r & 31)) << 3)) = pk;
+                    for (int u = 0; u < 4; ++u)
+                        v[u] = dequant_bias(acc[i][j][q * 4 + u], sa, sb,
+                                            has_bias ? __uint_as_float((uint32_t)braw[j][q][u >> 1][u & 1] << 16) : 0.f);
+                    f(i * 32 + frow, j * 8 + q * 2 + fhalf, v);
                 }
-        }
+            }
+    }
+};
+
+// 16 x 16 x 128 MFMAs: lane l holds D[row0 + 16 i + l % 16][col0 + 16 j + 4 (l / 16) + u] in
+// element u of acc[i][j]; braw[j][u / 2][u % 2] = bias[col0 + 16 j + 4 (l / 16) + u].
+struct Quads16 {
+    const f32x4 (&acc)[8][8];
+    const us2 (&braw)[8][2];
+    bool has_bias;
+    float sa, sb;
+    int lane;
+    template <int RLO, int RHI, class F>
+    __device__ __forceinline__ void visit(F &&f) const {
+        const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (i * 16 < RLO || i * 16 >= RHI) continue;
+                float v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    v[u] = dequant_bias(acc[i][j][u], sa, sb,
+                                        has_bias ? __uint_as_float((uint32_t)braw[j][u >> 1][u & 1] << 16) : 0.f);
+                f(i * 16 + r16, j * 4 + g, v);
+            }
+    }
+};
+
+// Epilogue of the pipelined kernels.  Each wave scales, adds the bias and rounds its 128 x 128
+// sub-tile into its own 32 KB of LDS, then writes whole rows with 16-byte streaming
+// (nontemporal) stores.  bf16: one pass, row r at r * 256, 8-byte slot s (columns 4 s .. 4 s + 3)
+// stored at slot s ^ (r & 31).  float32: two passes of 64 rows, row r at r * 512, 16-byte slot s
+// at s ^ (r & 31).  Where D or ldd is not 16-byte aligned, or at the ragged right edge, the
+// elements are stored one by one.
+template <int OUT, class Q>
+__device__ __forceinline__ void epilogue_staged(const Q &quads, float ds, void *__restrict__ D, int64_t ldd,
+                                                int M, int N, int row0, int col0, int lane, uint8_t *wlds,
+                                                OutQuant oq) {
+    constexpr int kElemsPer16 = OUT == 0 ? 8 : OUT == 1 ? 4 : 16;
+    const bool vec_ok = ((reinterpret_cast<uintptr_t>(D) & 15u) == 0) && (ldd % kElemsPer16 == 0);
+    if constexpr (OUT == 0) {
+        quads.template visit<0, 128>([&](int r, int sl, const float (&v)[4]) {
+            const u32x2 pk = {f32x2_to_bf16x2_rne(v[0], v[1]), f32x2_to_bf16x2_rne(v[2], v[3])};
+            *reinterpret_cast<u32x2 *>(wlds + r * 256 + ((sl ^ (r & 31)) << 3)) = pk;
+        });
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
         __builtin_amdgcn_wave_barrier();
         // 16-byte chunk ch of row r = slots 2 ch, 2 ch + 1, stored at (2 ch) ^ x and (2 ch + 1) ^ x
@@ -193,26 +241,14 @@ __device__ __forceinline__ void epilogue_staged(const f32x16 (&acc)[4][4], float
             }
         }
     } else if constexpr (OUT == 1) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float bv[4][4];
-                load_bias(j, bv);
-#pragma unroll
-                for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int i = h * 2 + ii;
-                        const int r = ii * 32 + frow, sl = j * 8 + q * 2 + fhalf;
-                        u32x4 pk;
-                        pk.x = __float_as_uint(dequant_bias(acc[i][j][q * 4 + 0], sa, sb, bv[q][0]));
-                        pk.y = __float_as_uint(dequant_bias(acc[i][j][q * 4 + 1], sa, sb, bv[q][1]));
-                        pk.z = __float_as_uint(dequant_bias(acc[i][j][q * 4 + 2], sa, sb, bv[q][2]));
-                        pk.w = __float_as_uint(dequant_bias(acc[i][j][q * 4 + 3], sa, sb, bv[q][3]));
-                        *reinterpret_cast<u32x4 *>(wlds + r * 512 + ((sl ^ (r & 31)) << 4)) = pk;
-                    }
-            }
+        auto pass = [&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            quads.template visit<h * 64, h * 64 + 64>([&](int r, int sl, const float (&v)[4]) {
+                const int rr = r - h * 64;
+                const u32x4 pk = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                  __float_as_uint(v[3])};
+                *reinterpret_cast<u32x4 *>(wlds + rr * 512 + ((sl ^ (rr & 31)) << 4)) = pk;
+            });
             __builtin_amdgcn_s_waitcnt(0xC07F);
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -235,7 +271,9 @@ __device__ __forceinline__ void epilogue_staged(const f32x16 (&acc)[4][4], float
             // the second pass overwrites what this pass read
             __builtin_amdgcn_s_waitcnt(0xC07F);
             __builtin_amdgcn_wave_barrier();
-        }
+        };
+        pass(std::integral_constant<int, 0>{});
+        pass(std::integral_constant<int, 1>{});
     } else {
         // FP8: 128 rows x 128 bytes = 16 KB; row r at r * 128, 4-byte slot s (columns 4 s ..
         // 4 s + 3) stored at slot s ^ (r & 31).
@@ -245,44 +283,26 @@ __device__ __forceinline__ void epilogue_staged(const f32x16 (&acc)[4][4], float
         // them with the clamp + hardware conversion alone (one wave-uniform branch).
         constexpr int F = OUT - 2;
         uint32_t amag = 0;
+        quads.template visit<0, 128>([&](int, int, const float (&v)[4]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float bv[4][4];
-            load_bias(j, bv);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        amag = max(amag, __float_as_uint(dequant_bias(acc[i][j][q * 4 + u], sa, sb, bv[q][u])) &
-                                             0x7FFFFFFFu);
-        }
+            for (int u = 0; u < 4; ++u) amag = max(amag, __float_as_uint(v[u]) & 0x7FFFFFFFu);
+        });
         amag = __builtin_amdgcn_readfirstlane(wave_max_u32(amag));   // wave-uniform
         if (lane == 0) fold_amax_bits(oq.amax, amag);
         auto stage = [&](auto fast_tag) {
             constexpr bool kFast = decltype(fast_tag)::value;
+            quads.template visit<0, 128>([&](int r, int sl, const float (&v)[4]) {
+                float y[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float bv[4][4];
-                load_bias(j, bv);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int r = i * 32 + frow, sl = j * 8 + q * 2 + fhalf;
-                        float y[4];
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) y[u] = dequant_bias(acc[i][j][q * 4 + u], sa, sb, bv[q][u]) * ds;
-                        uint32_t w;
-                        if constexpr (kFast)
-                            w = pack4<F>(clamp_fmt<F>(y[0]), clamp_fmt<F>(y[1]), clamp_fmt<F>(y[2]), clamp_fmt<F>(y[3]));
-                        else
-                            w = encode_exact<F>(y[0]) | (encode_exact<F>(y[1]) << 8) | (encode_exact<F>(y[2]) << 16) |
-                                (encode_exact<F>(y[3]) << 24);
-                        *reinterpret_cast<uint32_t *>(wlds + r * 128 + ((sl ^ (r & 31)) << 2)) = w;
-                    }
-            }
+                for (int u = 0; u < 4; ++u) y[u] = v[u] * ds;
+                uint32_t w;
+                if constexpr (kFast)
+                    w = pack4<F>(clamp_fmt<F>(y[0]), clamp_fmt<F>(y[1]), clamp_fmt<F>(y[2]), clamp_fmt<F>(y[3]));
+                else
+                    w = encode_exact<F>(y[0]) | (encode_exact<F>(y[1]) << 8) | (encode_exact<F>(y[2]) << 16) |
+                        (encode_exact<F>(y[3]) << 24);
+                *reinterpret_cast<uint32_t *>(wlds + r * 128 + ((sl ^ (r & 31)) << 2)) = w;
+            });
         };
         if (scale_is_plain(ds) && amag <= 0x7F800000u)
             stage(std::true_type{});
@@ -643,7 +663,208 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias_pipe(const uint8_t *_
 #pragma unroll
             for (int u = 0; u < 4; ++u)
                 braw[j][q][u >> 1][u & 1] = bsrc[has_bias ? min(col0 + j * 32 + q * 8 + bhalf * 4 + u, N - 1) : 0];
-    epilogue_staged<OUT>(acc, sa, sb, ds, has_bias, braw, D, ldd, M, N, m0 + wm * 128, col0, lane, wl, oq);
+    epilogue_staged<OUT>(Quads32{acc, braw, has_bias, sa, sb, lane}, ds, D, ldd, M, N, m0 + wm * 128, col0, lane, wl, oq);
+}
+
+// ------------------------------------------------------------------------------------------
+// k_gemm_pipe16: the hot-path kernel for K % 256 == 0.  Same 256 x 256 block tile and 2 x 2 waves
+// of 128 x 128, but built on v_mfma_f32_16x16x128_f8f6f4 (8 x 8 MFMA tiles per wave), which under
+// the chip's power limit sustains more FP8 throughput than the 32 x 32 x 64 form.  One K step is
+// 128 bytes; A and B have separate 32 KB LDS slots (256 rows x 128 bytes), two of each:
+//   step j computes with A_j (its fragments read one 16-row block ahead of the MFMAs) and B_j
+//   (whose fragments were read into registers during step j-1), while reading the fragments of
+//   B_{j+1} and, last, A_{j+1}'s first block.  B_j's slot is free once its fragments are in
+//   registers, so B runs a step further ahead than A: the loads of step j are A_{j+1} (into the
+//   slot A_{j-1} used) and B_{j+2} (into B_j's slot), 16 per wave, issued four after the previous
+//   step's barrier and four in each of the first three 16-row blocks; step j waits for them once,
+//   before its last block, with one barrier (which also frees A_j's and B_{j+1}'s slots).
+// Loads into LDS are buffer loads (per-tile descriptors, 32-bit lane offsets, the K step in the
+// scalar offset); a load index past the last K step is clamped to it (the extra loads at the end
+// refill free slots and are never read).  LDS rows are 128 bytes; 16-byte chunk c of row r sits
+// at c ^ ((r / 2) % 8), which keeps the fragment reads free of bank conflicts.  The epilogue is
+// the staged one above.  k_gemm_small16 does the same MFMAs in the same K order, so the two give
+// identical bits; they do not match the 32 x 32 x 64 kernels bit for bit (the MFMA sums 128
+// products per instruction), so a GEMM takes all its tiles from one family: the launcher picks
+// the family from K and the row strides alone, never from M or N.
+// ------------------------------------------------------------------------------------------
+namespace {
+constexpr int kQK = 128;                          // K bytes per step
+constexpr int kQSlice = 256 * kQK;                // one operand slot: 256 rows x 128 bytes
+constexpr int kFam16K = 2 * kQK;                  // K multiple for the 16 x 16 x 128 family
+__device__ __forceinline__ int qswz(int r) { return (r >> 1) & 7; }
+}  // namespace
+
+// vmcnt(0) and lgkmcnt(0): every load into LDS and every LDS read of this wave has completed
+#define FP8DS_WAIT_ALL() __builtin_amdgcn_s_waitcnt(0x0070)
+
+template <int FA, int FB, int OUT>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_pipe16(const uint8_t *__restrict__ A, int64_t lda,
+                                                             const uint8_t *__restrict__ B, int64_t ldb,
+                                                             const float *__restrict__ a_sinv,
+                                                             const float *__restrict__ b_sinv,
+                                                             const uint16_t *__restrict__ bias,
+                                                             void *__restrict__ D, int64_t ldd, int M, int N,
+                                                             int K, int tiles_m, int tiles_n, OutQuant oq) {
+    if constexpr (OUT >= 2)
+        if (blockIdx.x == 0 && threadIdx.x == 0 && oq.scale_inv_out != nullptr) *oq.scale_inv_out = 1.0f / *oq.scale;
+    const float sa = *a_sinv, sb = *b_sinv;
+    float ds = 0.f;
+    if constexpr (OUT >= 2) ds = *oq.scale;
+    __shared__ __align__(16) uint8_t sa0[kQSlice];
+    __shared__ __align__(16) uint8_t sa1[kQSlice];
+    __shared__ __align__(16) uint8_t sb0[kQSlice];
+    __shared__ __align__(16) uint8_t sb1[kQSlice];
+
+    int tm, tn;
+    block_tile(tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // Load i (0-7) of wave w fills the slot's 1 KB block 4 i + w = rows 8 (4 i + w) .. +7: lane l
+    // takes row 32 i + 8 w + l / 8, stored chunk l % 8, i.e. source chunk (l % 8) ^ qswz(row),
+    // where qswz(row) = (4 w + l / 16) % 8 for every i.
+    const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
+    const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(A + (int64_t)m0 * lda), (short)0, (int)(rows_a * lda), kBufDesc3);
+    const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(B + (int64_t)n0 * ldb), (short)0, (int)(rows_b * ldb), kBufDesc3);
+    const int lrow = wave * 8 + (lane >> 3);
+    const int lsc = (lane & 7) ^ (((lane >> 4) + 4 * wave) & 7);
+    uint32_t va[8], vb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = i * 32 + lrow;
+        va[i] = (uint32_t)(min(r, rows_a - 1) * lda + lsc * 16);
+        vb[i] = (uint32_t)(min(r, rows_b - 1) * ldb + lsc * 16);
+    }
+    const int nk = K / kQK;   // even
+#define FP8DS_LD_A(SA_, j, i)                                                                              \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (__attribute__((address_space(3))) void *)((SA_) + ((i) * 4 + wave) * 1024), \
+                                             16, va[i], (uint32_t)(min((j), nk - 1) * kQK), 0, 0);
+#define FP8DS_LD_B(SB_, j, i)                                                                              \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (__attribute__((address_space(3))) void *)((SB_) + ((i) * 4 + wave) * 1024), \
+                                             16, vb[i], (uint32_t)(min((j), nk - 1) * kQK), 0, 0);
+    // loads n0 .. n1-1 of a step's 16, in the order A0 B0 A1 B1 ... (A step jA, B step jB)
+#define FP8DS_LDS(n0, n1, SA_, SB_, jA, jB)                                                                \
+    _Pragma("unroll") for (int n = (n0); n < (n1); ++n) {                                                 \
+        if (n & 1) { FP8DS_LD_B(SB_, jB, n >> 1) } else { FP8DS_LD_A(SA_, jA, n >> 1) }                    \
+    }
+
+    f32x4 acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Operand fragment of a 16-row MFMA tile: lane l supplies row l % 16 and K bytes
+    // [32 (l / 16), +32) of the step, two 16-byte reads.
+    const int r16 = lane & 15, g = lane >> 4;
+    const int oc0 = r16 * kQK + (((2 * g) ^ qswz(r16)) << 4);
+    const int oc1 = r16 * kQK + (((2 * g + 1) ^ qswz(r16)) << 4);
+    const int offa = wm * 128 * kQK, offb = wn * 128 * kQK;
+    auto ld = [&](const uint8_t *p) -> i32x8 {
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(p + oc0);
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(p + oc1);
+        i32x8 r;
+        r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+        r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+        return r;
+    };
+    i32x8 fb0[8], fb1[8], fa0, fa1;
+#define FP8DS_MF(FBC, FA_, i)                                                                              \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                                         \
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(FBC[j], FA_, acc[i][j], FB, FA, 0, 0, 0, 0);
+    // scheduling of one 16-row block: its 8 MFMAs, with NRD fragment reads and NLD loads placed
+    // one (loads: up to two) after each MFMA from the first on
+#define FP8DS_SG(NRD, NLD)                                                                                 \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                                       \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                \
+        if (q < (NRD)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                 \
+        if (q < (NLD)) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                 \
+        if (q + 8 < (NLD)) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                             \
+    }
+    // 16-row block i (0-6) of step j: read A frag i+1 and, in blocks 0-3, the next step's B frags
+    // 2i and 2i+1; issue loads N0 .. N1-1 of step j; MFMAs with A frag i
+#define FP8DS_BLK(i, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, FA_C, FA_N, N0, N1)                     \
+    {                                                                                                     \
+        FA_N = ld((SA_CUR) + offa + ((i) + 1) * 16 * kQK);                                                \
+        if ((i) < 4) {                                                                                    \
+            FBN[2 * (i)] = ld((SB_NXT) + offb + (2 * (i)) * 16 * kQK);                                    \
+            FBN[2 * (i) + 1] = ld((SB_NXT) + offb + (2 * (i) + 1) * 16 * kQK);                            \
+        }                                                                                                 \
+        FP8DS_LDS(N0, N1, SA_NXT, SB_FREE, (j) + 1, (j) + 2)                                              \
+        FP8DS_MF(FBC, FA_C, i)                                                                            \
+        FP8DS_SG(((i) < 4 ? 6 : 2), ((N1) - (N0)))                                                        \
+        __builtin_amdgcn_sched_barrier(0);                                                                \
+    }
+    // Step j: A_j in SA_CUR, A_{j+1} in SA_NXT, B_{j+1} in SB_NXT, B_j's slot SB_FREE, B_j's
+    // fragments in FBC.  Loads 4-15 of step j in blocks 0-2; wait + barrier; then block 7 reads the
+    // next step's A frag 0 and issues loads 0-3 of step j+1 (A_{j+2} into SA_CUR, B_{j+3} into
+    // SB_NXT), both slots freed by the barrier.
+#define FP8DS_STEP16(j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN)                                         \
+    {                                                                                                     \
+        __builtin_amdgcn_sched_barrier(0);                                                                \
+        FP8DS_BLK(0, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, fa0, fa1, 4, 8)                         \
+        FP8DS_BLK(1, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, fa1, fa0, 8, 12)                        \
+        FP8DS_BLK(2, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, fa0, fa1, 12, 16)                       \
+        FP8DS_BLK(3, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, fa1, fa0, 16, 16)                       \
+        FP8DS_BLK(4, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, fa0, fa1, 16, 16)                       \
+        FP8DS_BLK(5, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, fa1, fa0, 16, 16)                       \
+        FP8DS_BLK(6, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, fa0, fa1, 16, 16)                       \
+        FP8DS_WAIT_ALL();                                                                                 \
+        FP8DS_BARRIER();                                                                                  \
+        __builtin_amdgcn_sched_barrier(0);                                                                \
+        fa0 = ld((SA_NXT) + offa);                                                                        \
+        FP8DS_LDS(0, 4, SA_CUR, SB_NXT, (j) + 2, (j) + 3)                                                 \
+        FP8DS_MF(FBC, fa1, 7)                                                                             \
+        FP8DS_SG(2, 4)                                                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                                \
+    }
+    // prologue: A_0 and B_0, then B_1; wait for step 0, read B_0's fragments and A frag 0; wait
+    // for B_1 and for every wave's reads of B_0's slot; issue loads 0-3 of step 0
+    FP8DS_LDS(0, 16, sa0, sb0, 0, 0)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { FP8DS_LD_B(sb1, 1, i) }
+    __builtin_amdgcn_sched_barrier(0);
+    FP8DS_WAIT_VM(8);
+    FP8DS_BARRIER();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fb0[j] = ld(sb0 + offb + j * 16 * kQK);
+    fa0 = ld(sa0 + offa);
+    FP8DS_WAIT_ALL();
+    FP8DS_BARRIER();
+    __builtin_amdgcn_sched_barrier(0);
+    FP8DS_LDS(0, 4, sa1, sb0, 1, 2)
+    __builtin_amdgcn_sched_barrier(0);
+    // A_j and B_j in slot j % 2, B_j's fragments in fb[j % 2]
+    for (int j = 0; j < nk; j += 2) {
+        FP8DS_STEP16(j, sa0, sa1, sb1, sb0, fb0, fb1)
+        FP8DS_STEP16(j + 1, sa1, sa0, sb0, sb1, fb1, fb0)
+    }
+#undef FP8DS_STEP16
+#undef FP8DS_BLK
+#undef FP8DS_SG
+#undef FP8DS_MF
+#undef FP8DS_LDS
+#undef FP8DS_LD_A
+#undef FP8DS_LD_B
+    __syncthreads();   // every load has landed and every wave is done reading the slots
+    uint8_t *wl = wave == 0 ? sa0 : wave == 1 ? sa1 : wave == 2 ? sb0 : sb1;
+    // the bias of the 32 columns this lane holds, two values per register, loaded together
+    // (unconditional loads: without a bias they read the first two bytes of a_sinv)
+    const bool has_bias = bias != nullptr;
+    const uint16_t *bsrc = has_bias ? bias : reinterpret_cast<const uint16_t *>(a_sinv);
+    const int col0 = n0 + wn * 128;
+    us2 braw[8][2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            braw[j][u >> 1][u & 1] = bsrc[has_bias ? min(col0 + j * 16 + g * 4 + u, N - 1) : 0];
+    epilogue_staged<OUT>(Quads16{acc, braw, has_bias, sa, sb, lane}, ds, D, ldd, M, N, m0 + wm * 128, col0, lane, wl, oq);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -781,6 +1002,114 @@ __global__ __launch_bounds__(64) void k_gemm_small(const uint8_t *__restrict__ A
     }
 }
 
+// k_gemm_small16: the small-problem kernel of the 16 x 16 x 128 family (K % 256 == 0).  One wave
+// per 64 x 64 tile, 4 x 4 MFMA tiles of 16 x 16; each lane loads its operand fragments straight
+// into registers, three 128-byte K steps ahead.  The MFMAs, their operand order and K order and
+// the epilogue arithmetic are those of k_gemm_pipe16, so the two give the same bits.
+template <int FA, int FB, int OUT>
+__global__ __launch_bounds__(64) void k_gemm_small16(const uint8_t *__restrict__ A, int64_t lda,
+                                                     const uint8_t *__restrict__ B, int64_t ldb,
+                                                     const float *__restrict__ a_sinv, const float *__restrict__ b_sinv,
+                                                     const uint16_t *__restrict__ bias, void *__restrict__ D,
+                                                     int64_t ldd, int M, int N, int K, int tiles_n, OutQuant oq) {
+    if constexpr (OUT >= 2)
+        if (blockIdx.x == 0 && threadIdx.x == 0 && oq.scale_inv_out != nullptr) *oq.scale_inv_out = 1.0f / *oq.scale;
+    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - (blockIdx.x / tiles_n) * tiles_n;
+    const int m0 = tm * kSmallTile, n0 = tn * kSmallTile;
+    const int lane = threadIdx.x, r16 = lane & 15, g = lane >> 4;
+    // lane l supplies row l % 16 of each 16-row operand tile and bytes [32 (l / 16), +32) of the
+    // step; rows past M / N read the last row (their values are never stored or counted)
+    const uint8_t *pa[4], *pb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        pa[i] = A + (int64_t)min(m0 + i * 16 + r16, M - 1) * lda + g * 32;
+        pb[i] = B + (int64_t)min(n0 + i * 16 + r16, N - 1) * ldb + g * 32;
+    }
+    auto ld32 = [](const uint8_t *p) -> i32x8 {
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(p);
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(p + 16);
+        i32x8 r;
+        r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+        r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+        return r;
+    };
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // scales, output scale and bias before the K loop; bias loads unconditional (see k_gemm_small)
+    const float sa = *a_sinv, sb = *b_sinv;
+    float ds = 0.f;
+    if constexpr (OUT >= 2) ds = *oq.scale;
+    const bool has_bias = bias != nullptr;
+    const uint16_t *bsrc = has_bias ? bias : reinterpret_cast<const uint16_t *>(a_sinv);
+    uint32_t braw[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) braw[j][u] = bsrc[has_bias ? min(n0 + j * 16 + g * 4 + u, N - 1) : 0];
+    const int nk = K / kQK;
+#define FP8DS_SLOAD(FA_, FB_, kt)                                                                          \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                       \
+        FA_[i] = ld32(pa[i] + (int64_t)(kt) * kQK);                                                       \
+        FB_[i] = ld32(pb[i] + (int64_t)(kt) * kQK);                                                       \
+    }
+#define FP8DS_SMFMA(FA_, FB_)                                                                              \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                         \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                         \
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(FB_[j], FA_[i], acc[i][j], FB, FA, 0, 0, 0, 0);
+    // unconditional loads, step index clamped (see k_gemm_small)
+    i32x8 a0[4], b0[4], a1[4], b1[4], a2[4], b2[4];
+    FP8DS_SLOAD(a0, b0, 0)
+    FP8DS_SLOAD(a1, b1, min(1, nk - 1))
+    FP8DS_SLOAD(a2, b2, min(2, nk - 1))
+    int kt = 0;
+    for (; kt + 3 <= nk; kt += 3) {
+        FP8DS_SMFMA(a0, b0)
+        FP8DS_SLOAD(a0, b0, min(kt + 3, nk - 1))
+        FP8DS_SMFMA(a1, b1)
+        FP8DS_SLOAD(a1, b1, min(kt + 4, nk - 1))
+        FP8DS_SMFMA(a2, b2)
+        FP8DS_SLOAD(a2, b2, min(kt + 5, nk - 1))
+    }
+    // the last nk % 3 steps, already in a0, a1 in K order
+    if (kt < nk) { FP8DS_SMFMA(a0, b0) }
+    if (kt + 1 < nk) { FP8DS_SMFMA(a1, b1) }
+#undef FP8DS_SLOAD
+#undef FP8DS_SMFMA
+    // epilogue, element by element: lane l holds D[m0 + 16 i + l % 16][n0 + 16 j + 4 (l / 16) + u]
+    // in element u of acc[i][j]
+    uint32_t amag = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = m0 + i * 16 + r16;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int col = n0 + j * 16 + g * 4 + u;
+                const float b = has_bias ? __uint_as_float(braw[j][u] << 16) : 0.f;
+                const float v = dequant_bias(acc[i][j][u], sa, sb, b);
+                if (row < M && col < N) {
+                    const int64_t o = (int64_t)row * ldd + col;
+                    if constexpr (OUT == 0) {
+                        reinterpret_cast<uint16_t *>(D)[o] = f32_to_bf16_rne(v);
+                    } else if constexpr (OUT == 1) {
+                        reinterpret_cast<float *>(D)[o] = v;
+                    } else {
+                        amag = max(amag, __float_as_uint(v) & 0x7FFFFFFFu);
+                        reinterpret_cast<uint8_t *>(D)[o] = (uint8_t)encode_exact<OUT - 2>(v * ds);
+                    }
+                }
+            }
+    }
+    if constexpr (OUT >= 2) {
+        amag = wave_max_u32(amag);
+        if (lane == 0) fold_amax_bits(oq.amax, amag);
+    }
+}
+
 // D = bias broadcast (K == 0): no products at all.
 template <int OUT>
 __global__ __launch_bounds__(256) void k_bias_only(const uint16_t *__restrict__ bias, void *__restrict__ D,
@@ -837,11 +1166,20 @@ hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64
     const bool k64 = (K % kPK) == 0;
     const bool pipe = k64 && lda < kPipeMaxLd && ldb < kPipeMaxLd;
     const bool small = k64 && (int64_t)tiles_m * tiles_n < kSmallTiles;
+    // the 16 x 16 x 128 family (k_gemm_pipe16 / k_gemm_small16, identical bits) for K % 256 == 0;
+    // the choice depends on K and the strides only, so every N-chunk of a GEMM takes the same one
+    const bool fam16 = (K % kFam16K) == 0 && pipe;
     const int stiles_n = (int)((N + kSmallTile - 1) / kSmallTile);
     dim3 sgrid((unsigned)(((M + kSmallTile - 1) / kSmallTile) * stiles_n));
 #define FP8DS_GEMM(FA_, FB_, O_)                                                                           \
     do {                                                                                                   \
-        if (small)                                                                                         \
+        if (fam16 && small)                                                                                \
+            k_gemm_small16<FA_, FB_, O_><<<sgrid, dim3(64), 0, st>>>(                                      \
+                A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, stiles_n, oq);       \
+        else if (fam16)                                                                                    \
+            k_gemm_pipe16<FA_, FB_, O_><<<grid, dim3(kThreads), 0, st>>>(                                  \
+                A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, tiles_m, tiles_n, oq); \
+        else if (small)                                                                                    \
             k_gemm_small<FA_, FB_, O_><<<sgrid, dim3(64), 0, st>>>(                                        \
                 A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, stiles_n, oq);       \
         else if (pipe)                                                                                     \

@@ -255,9 +255,11 @@ def test_small_problem_kernel_matches_large_tile_kernel(shape, out_dtype):
                                    (513, 1000, 576)])
 @pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0)])
 def test_gemm_pipelined_path_shapes(shape, fa, fb):
-    """K a multiple of 64 takes the pipelined kernel: 1 to 9 K slices (prologue, steady state and
-    remainder loop), ragged M and N, against the oracle; and the same output as the general
-    kernel would give (checked through a K-padded call that the general kernel handles)."""
+    """K a multiple of 64 (1 to 9 slices of 64 bytes; these few-tile shapes run the register-fed
+    small-problem kernels), ragged M and N, against the oracle.  With K % 256 != 0 the 32 x 32 x 64
+    family runs, whose output must equal the general kernel's bit for bit (checked through a
+    K-padded call that the general kernel handles); K % 256 == 0 runs the 16 x 16 x 128 family,
+    whose MFMAs sum 128 products at once, so there only the oracle tolerance applies."""
     M, N, K = shape
     print(f"gemm pipe fa={fa} fb={fb} M={M} N={N} K={K}", flush=True)
     A8 = _codes(S.seed_for(23, fa), (M, K), fa, 2.0)
@@ -271,12 +273,40 @@ def test_gemm_pipelined_path_shapes(shape, fa, fb):
     # K + 16 zero columns: same products, general kernel (K % 64 != 0) -> identical bits
     pad = np.zeros((M, 16), np.uint8), np.zeros((N, 16), np.uint8)
     Dg = _run(np.hstack([A8, pad[0]]), fa, 0.5, np.hstack([B8, pad[1]]), fb, 0.25, bias, 1)
-    assert torch.equal(D.view(torch.int32), Dg.view(torch.int32))
+    gemm_close(to_f64(Dg), R, bf16_out=False)
+    if K % 256 != 0:
+        assert torch.equal(D.view(torch.int32), Dg.view(torch.int32))
+
+
+@pytest.mark.parametrize("shape", [(1100, 2300, 256), (1500, 1800, 512), (2304, 1041, 1280), (4097, 700, 768)])
+@pytest.mark.parametrize("fa,fb", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_gemm_fam16_large_tile_kernel(shape, fa, fb):
+    """K % 256 == 0 with 40 or more 256 x 256 tiles runs the 16 x 16 x 128 pipelined kernel: 2 to
+    10 K steps of 128 bytes, ragged M and N (partial tiles at both edges), every format pair,
+    float32 and bfloat16 output against the oracle on sampled rows (the ragged last rows
+    included); the same GEMM cut into four N-chunks (under 40 tiles each) runs the small-problem
+    kernel of the same family and must give the same bits."""
+    M, N, K = shape
+    print(f"gemm fam16 fa={fa} fb={fb} M={M} N={N} K={K}", flush=True)
+    A8 = _codes(S.seed_for(26, fa), (M, K), fa, 2.0)
+    B8 = _codes(S.seed_for(27, fb), (N, K), fb, 2.0)
+    bias = S.normal_bf16(S.seed_for(28, 0), (N,), 0.1)
+    rows = np.unique(np.concatenate([(S.uniform(S.seed_for(28, 1), 0, 48) * M).astype(np.int64),
+                                     np.arange(M - 3, M)]))
+    Rr, _ = oracle.gemm_bias_sampled(A8, fa, 0.5, B8, fb, 0.25, bias, rows, [0])
+    D = _run(A8, fa, 0.5, B8, fb, 0.25, bias, 1)
+    gemm_close(to_f64(D)[rows], Rr, bf16_out=False)
+    Db = _run(A8, fa, 0.5, B8, fb, 0.25, bias, 0)
+    gemm_close(to_f64(Db)[rows], Rr, bf16_out=True)
+    Dc = torch.zeros_like(D)
+    F.fp8_gemm_bias_chunked(_u8(A8), fa, scalar(0.5), _u8(B8), fb, scalar(0.25), bf16_dev(bias), Dc, 4, None)
+    torch.cuda.synchronize()
+    assert torch.equal(Dc.view(torch.int32), D.view(torch.int32))
 
 
 @pytest.mark.parametrize("sa,sb", [(1.2345678, 1.0), (1.01171875, 1.0), (0.70710677, 2.0 ** -120), (1.9, 2.0 ** 110)])
-@pytest.mark.parametrize("shape", [(256, 64, 64), (1280, 2048, 64), (300, 200, 48)],
-                         ids=["small-kernel", "pipelined-kernel", "general-kernel"])
+@pytest.mark.parametrize("shape", [(256, 64, 64), (1280, 2048, 64), (300, 200, 48), (256, 64, 256), (1280, 2048, 256)],
+                         ids=["small-kernel", "pipelined-kernel", "general-kernel", "small16-kernel", "pipe16-kernel"])
 def test_bf16_output_rounding_is_exact(shape, sa, sb):
     """One nonzero product per output (row code times column code, every E4M3 code on both
     sides), so the float32 value before the bfloat16 store is known exactly: the stored bits

@@ -65,7 +65,8 @@ def _exact_operands(seed, M, N, K):
 
 
 @pytest.mark.parametrize("d_fmt", [F.E4M3, F.E5M2])
-@pytest.mark.parametrize("K", [192, 80])   # the pipelined kernel (K % 64 == 0) and the general one
+# the 32 x 32 x 64 small kernel (K % 64 == 0), the general one, the 16 x 16 x 128 small kernel
+@pytest.mark.parametrize("K", [192, 80, 256])
 def test_gemm_fp8_out_exact_arithmetic(d_fmt, K):
     """Codes in {0, +-0.5, +-1, +-2}, power-of-two inverse scales and quarter-integer bias: every
     float32 partial sum is exact, so codes, amax and inverse scale must match the oracle bit
@@ -100,7 +101,8 @@ def test_gemm_fp8_out_parity(fa, fb, d_fmt, shape):
     assert f32_bits(sinv)[0] == f32_bits(oracle.scale_inv(ds))[0]
 
 
-@pytest.mark.parametrize("shape", [(300, 520, 272), (513, 257, 1040), (600, 900, 208), (77, 1000, 64)])
+@pytest.mark.parametrize("shape", [(300, 520, 272), (513, 257, 1040), (600, 900, 208), (77, 1000, 64),
+                                   (1100, 2300, 512), (1300, 2100, 320)])
 @pytest.mark.parametrize("d_fmt", [F.E4M3, F.E5M2])
 def test_gemm_fp8_out_equals_encoded_fp32_output(shape, d_fmt):
     """The FP8 output is the float32 output of the same GEMM encoded with the output scale
