@@ -59,18 +59,28 @@ constexpr int kLdsBytes = 2 * (kLdsA + kLdsB);
 
 __device__ __forceinline__ int lds_chunk(int row, int c) { return c ^ (row & 7) ^ ((row >> 3) & 1); }
 
-// Tile of this block: XCD-contiguous ranges, walked in groups of kGroupM tile-rows.
-__device__ __forceinline__ void block_tile(int tiles_m, int tiles_n, int &tm, int &tn) {
-    const int nwg = tiles_m * tiles_n;
-    const int bid = blockIdx.x;
+// Tile of this block.  The tile-rows are taken in bands of band_rows (all of them when the
+// operands fit in the chip's 256 MB Infinity Cache), one band after the other in block order;
+// inside a band each XCD (blocks are dealt round-robin to the 8 XCDs) works on a contiguous range
+// of tiles, walked in groups of kGroupM tile-rows for L2 reuse.  When A and B together exceed the
+// Infinity Cache, finishing a band of A rows against all of B before the next keeps the A rows
+// every XCD re-reads cache-resident while B streams through (measured on the QKV forward GEMM,
+// 327 MB of operands: 5% faster with bands of 8 tile-rows, no change where the operands fit).
+__device__ __forceinline__ void block_tile(int tiles_m, int tiles_n, int band_rows, int &tm, int &tn) {
+    const int per = band_rows * tiles_n;
+    const int band = (int)blockIdx.x / per;
+    const int rows0 = band * band_rows;
+    const int rows = min(band_rows, tiles_m - rows0);
+    const int bid = (int)blockIdx.x - band * per;
+    const int nwg = rows * tiles_n;
     const int xcd = bid & 7, local = bid >> 3;
     const int q8 = nwg >> 3, r8 = nwg & 7;
     const int tile = (xcd < r8) ? xcd * (q8 + 1) + local : r8 * (q8 + 1) + (xcd - r8) * q8 + local;
     const int group = tile / (kGroupM * tiles_n);
     const int first_m = group * kGroupM;
-    const int gm = min(tiles_m - first_m, kGroupM);
+    const int gm = min(rows - first_m, kGroupM);
     const int in_group = tile - group * kGroupM * tiles_n;
-    tm = first_m + in_group % gm;
+    tm = rows0 + first_m + in_group % gm;
     tn = in_group / gm;
 }
 }  // namespace
@@ -342,13 +352,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias(const uint8_t *__rest
                                                            const float *__restrict__ b_sinv,
                                                            const uint16_t *__restrict__ bias,
                                                            void *__restrict__ D, int64_t ldd, int M, int N,
-                                                           int K, int tiles_m, int tiles_n, OutQuant oq) {
+                                                           int K, int tiles_m, int tiles_n, int band_rows,
+                                                             OutQuant oq) {
     if constexpr (OUT >= 2)
         if (blockIdx.x == 0 && threadIdx.x == 0 && oq.scale_inv_out != nullptr) *oq.scale_inv_out = 1.0f / *oq.scale;
     __shared__ __align__(16) uint8_t smem[kLdsBytes];
 
     int tm, tn;
-    block_tile(tiles_m, tiles_n, tm, tn);
+    block_tile(tiles_m, tiles_n, band_rows, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -487,7 +498,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias_pipe(const uint8_t *_
                                                                 const float *__restrict__ b_sinv,
                                                                 const uint16_t *__restrict__ bias,
                                                                 void *__restrict__ D, int64_t ldd, int M, int N,
-                                                                int K, int tiles_m, int tiles_n, OutQuant oq) {
+                                                                int K, int tiles_m, int tiles_n, int band_rows,
+                                                             OutQuant oq) {
     if constexpr (OUT >= 2)
         if (blockIdx.x == 0 && threadIdx.x == 0 && oq.scale_inv_out != nullptr) *oq.scale_inv_out = 1.0f / *oq.scale;
     // scalars the epilogue needs, read before the K loop (uniform: scalar registers)
@@ -500,7 +512,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias_pipe(const uint8_t *_
     __shared__ __align__(16) uint8_t st3[kPStage];
 
     int tm, tn;
-    block_tile(tiles_m, tiles_n, tm, tn);
+    block_tile(tiles_m, tiles_n, band_rows, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -704,7 +716,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pipe16(const uint8_t *__re
                                                              const float *__restrict__ b_sinv,
                                                              const uint16_t *__restrict__ bias,
                                                              void *__restrict__ D, int64_t ldd, int M, int N,
-                                                             int K, int tiles_m, int tiles_n, OutQuant oq) {
+                                                             int K, int tiles_m, int tiles_n, int band_rows,
+                                                             OutQuant oq) {
     if constexpr (OUT >= 2)
         if (blockIdx.x == 0 && threadIdx.x == 0 && oq.scale_inv_out != nullptr) *oq.scale_inv_out = 1.0f / *oq.scale;
     const float sa = *a_sinv, sb = *b_sinv;
@@ -716,7 +729,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pipe16(const uint8_t *__re
     __shared__ __align__(16) uint8_t sb1[kQSlice];
 
     int tm, tn;
-    block_tile(tiles_m, tiles_n, tm, tn);
+    block_tile(tiles_m, tiles_n, band_rows, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -785,18 +798,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pipe16(const uint8_t *__re
         if (q < (NLD)) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                 \
         if (q + 8 < (NLD)) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                             \
     }
-    // 16-row block i (0-6) of step j: read A frag i+1 and, in blocks 0-3, the next step's B frags
-    // 2i and 2i+1; issue loads N0 .. N1-1 of step j; MFMAs with A frag i
+    // 16-row block i (0-6) of step j: read A frag i+1 and the next step's B frag i+1 (block 0 also
+    // B frag 0); issue loads N0 .. N1-1 of step j; MFMAs with A frag i
 #define FP8DS_BLK(i, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, FA_C, FA_N, N0, N1)                     \
     {                                                                                                     \
         FA_N = ld((SA_CUR) + offa + ((i) + 1) * 16 * kQK);                                                \
-        if ((i) < 4) {                                                                                    \
-            FBN[2 * (i)] = ld((SB_NXT) + offb + (2 * (i)) * 16 * kQK);                                    \
-            FBN[2 * (i) + 1] = ld((SB_NXT) + offb + (2 * (i) + 1) * 16 * kQK);                            \
-        }                                                                                                 \
+        if ((i) == 0) FBN[0] = ld((SB_NXT) + offb);                                                       \
+        FBN[(i) + 1] = ld((SB_NXT) + offb + ((i) + 1) * 16 * kQK);                                        \
         FP8DS_LDS(N0, N1, SA_NXT, SB_FREE, (j) + 1, (j) + 2)                                              \
         FP8DS_MF(FBC, FA_C, i)                                                                            \
-        FP8DS_SG(((i) < 4 ? 6 : 2), ((N1) - (N0)))                                                        \
+        FP8DS_SG(((i) == 0 ? 6 : 4), ((N1) - (N0)))                                                        \
         __builtin_amdgcn_sched_barrier(0);                                                                \
     }
     // Step j: A_j in SA_CUR, A_{j+1} in SA_NXT, B_{j+1} in SB_NXT, B_j's slot SB_FREE, B_j's
@@ -1170,6 +1181,9 @@ hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64
     // the choice depends on K and the strides only, so every N-chunk of a GEMM takes the same one
     const bool fam16 = (K % kFam16K) == 0 && pipe;
     const int stiles_n = (int)((N + kSmallTile - 1) / kSmallTile);
+    // bands of 8 tile-rows when the operands exceed the 256 MB Infinity Cache (block_tile)
+    constexpr int64_t kInfinityCache = INT64_C(256) << 20;
+    const int band_rows = (M * lda + N * ldb > kInfinityCache) ? 8 : tiles_m;
     dim3 sgrid((unsigned)(((M + kSmallTile - 1) / kSmallTile) * stiles_n));
 #define FP8DS_GEMM(FA_, FB_, O_)                                                                           \
     do {                                                                                                   \
@@ -1178,16 +1192,16 @@ hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64
                 A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, stiles_n, oq);       \
         else if (fam16)                                                                                    \
             k_gemm_pipe16<FA_, FB_, O_><<<grid, dim3(kThreads), 0, st>>>(                                  \
-                A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, tiles_m, tiles_n, oq); \
+                A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, tiles_m, tiles_n, band_rows, oq); \
         else if (small)                                                                                    \
             k_gemm_small<FA_, FB_, O_><<<sgrid, dim3(64), 0, st>>>(                                        \
                 A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, stiles_n, oq);       \
         else if (pipe)                                                                                     \
             k_gemm_bias_pipe<FA_, FB_, O_><<<grid, dim3(kThreads), 0, st>>>(                               \
-                A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, tiles_m, tiles_n, oq); \
+                A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, tiles_m, tiles_n, band_rows, oq); \
         else                                                                                               \
             k_gemm_bias<FA_, FB_, O_><<<grid, dim3(kThreads), 0, st>>>(                                    \
-                A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, tiles_m, tiles_n, oq); \
+                A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, tiles_m, tiles_n, band_rows, oq); \
     } while (0)
 #define FP8DS_GEMM_OUT(FA_, FB_)                                                                           \
     switch (out_dtype) {                                                                                   \

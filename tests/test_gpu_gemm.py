@@ -330,3 +330,24 @@ def test_bf16_output_rounding_is_exact(shape, sa, sb):
     assert nan.any() and np.isinf(v).any() == (sb > 1e30)
     assert np.all((got[nan] & 0x7FFF) > 0x7F80), "NaN products must store a NaN"
     assert np.array_equal(got[~nan], want[~nan])
+
+
+def test_gemm_banded_tile_order_covers_every_tile():
+    """Operands over 256 MiB (here 270 MB) make the 256 x 256 kernels take the tile-rows in bands of
+    8; with M = 8492 (34 tile-rows: bands of 8, 8, 8, 8 and 2) every output element must still be
+    written exactly as the oracle says: the output starts as NaN, none may remain, and sampled
+    rows from every band (the ragged last rows included) match the oracle."""
+    M, N, K = 8492, 8000, 16384
+    assert M * K + N * K > 256 << 20
+    print(f"gemm banded M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(S.seed_for(29, 0))
+    A8 = (rng.integers(0, 0x7F, (M, K), dtype=np.uint8) | (rng.integers(0, 2, (M, K), dtype=np.uint8) << 7))
+    B8 = (rng.integers(0, 0x7F, (N, K), dtype=np.uint8) | (rng.integers(0, 2, (N, K), dtype=np.uint8) << 7))
+    bias = S.normal_bf16(S.seed_for(29, 1), (N,), 1.0)
+    D = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    F.fp8_gemm_bias(_u8(A8), 0, scalar(2.0 ** -10), _u8(B8), 0, scalar(2.0 ** -8), bf16_dev(bias), D)
+    torch.cuda.synchronize()
+    assert not torch.isnan(D).any().item()
+    rows = np.array([0, 1, 2047, 2048, 4100, 6143, 6200, 8191, 8192, 8300, M - 2, M - 1])
+    Rr, _ = oracle.gemm_bias_sampled(A8, 0, 2.0 ** -10, B8, 0, 2.0 ** -8, bias, rows, [0])
+    gemm_close(to_f64(D)[rows], Rr, bf16_out=False)
