@@ -693,7 +693,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias_pipe(const uint8_t *_
 // Loads into LDS are buffer loads (per-tile descriptors, 32-bit lane offsets, the K step in the
 // scalar offset); a load index past the last K step is clamped to it (the extra loads at the end
 // refill free slots and are never read).  LDS rows are 128 bytes; 16-byte chunk c of row r sits
-// at c ^ ((r / 2) % 8), which keeps the fragment reads free of bank conflicts.  The epilogue is
+// at c ^ (r % 8) ^ ((r / 8) % 2): the 16 lanes of a fragment read that share a chunk then hit
+// distinct banks both as two groups of 8 rows and as one group of 16 (the bank-conflict counter
+// reads 0; c ^ ((r / 2) % 8), distinct only for 16, counted 7.6e7 conflict cycles per launch).  The epilogue is
 // the staged one above.  k_gemm_small16 does the same MFMAs in the same K order, so the two give
 // identical bits; they do not match the 32 x 32 x 64 kernels bit for bit (the MFMA sums 128
 // products per instruction), so a GEMM takes all its tiles from one family: the launcher picks
@@ -703,7 +705,7 @@ namespace {
 constexpr int kQK = 128;                          // K bytes per step
 constexpr int kQSlice = 256 * kQK;                // one operand slot: 256 rows x 128 bytes
 constexpr int kFam16K = 2 * kQK;                  // K multiple for the 16 x 16 x 128 family
-__device__ __forceinline__ int qswz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int qswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 }  // namespace
 
 // vmcnt(0) and lgkmcnt(0): every load into LDS and every LDS read of this wave has completed
@@ -737,14 +739,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pipe16(const uint8_t *__re
 
     // Load i (0-7) of wave w fills the slot's 1 KB block 4 i + w = rows 8 (4 i + w) .. +7: lane l
     // takes row 32 i + 8 w + l / 8, stored chunk l % 8, i.e. source chunk (l % 8) ^ qswz(row),
-    // where qswz(row) = (4 w + l / 16) % 8 for every i.
+    // where qswz(row) = (l / 8) ^ (w % 2) for every i.
     const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
     const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(A + (int64_t)m0 * lda), (short)0, (int)(rows_a * lda), kBufDesc3);
     const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(B + (int64_t)n0 * ldb), (short)0, (int)(rows_b * ldb), kBufDesc3);
     const int lrow = wave * 8 + (lane >> 3);
-    const int lsc = (lane & 7) ^ (((lane >> 4) + 4 * wave) & 7);
+    const int lsc = (lane & 7) ^ ((lane >> 3) ^ (wave & 1));
     uint32_t va[8], vb[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
