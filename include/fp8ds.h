@@ -163,7 +163,10 @@ int fp8_scale_update(float *amax_history, int64_t L, int64_t T, float *scale, fl
  * gives the bias.
  * The result of every element depends only on its own row of A and row of B, never on the
  * tile it falls in, so an N-chunked call sequence (offset B, bias and D pointers with the
- * full ldd) reproduces the unchunked output bit for bit.
+ * full ldd) reproduces the unchunked output bit for bit.  K and the row strides (never M or N)
+ * select the matrix-core instruction: 16 x 16 x 128 when K % 256 == 0 and lda, ldb < 8 MiB,
+ * 32 x 32 x 64 otherwise; the two can round the float32 sum differently in the last bit, so
+ * calls with different K or strides need not agree bit for bit.
  */
 int fp8_gemm_bias(const uint8_t *A, int fa, const float *a_scale_inv, int64_t lda,
                   const uint8_t *B, int fb, const float *b_scale_inv, int64_t ldb,
