@@ -30,7 +30,8 @@ def _run(A8, fa, sa, B8, fb, sb, bias_h, out_dtype):
     return D
 
 
-SHAPES = [(1, 1, 16), (37, 45, 48), (256, 256, 128), (300, 520, 272), (513, 257, 1040), (128, 256, 256)]
+SHAPES = [(1, 1, 16), (37, 45, 48), (256, 256, 128), (300, 520, 272), (513, 257, 1040), (128, 256, 256),
+          (1, 1, 256), (37, 45, 512), (300, 520, 1024)]
 
 
 @pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (0, 1), (1, 1)])
@@ -278,7 +279,8 @@ def test_gemm_pipelined_path_shapes(shape, fa, fb):
         assert torch.equal(D.view(torch.int32), Dg.view(torch.int32))
 
 
-@pytest.mark.parametrize("shape", [(1100, 2300, 256), (1500, 1800, 512), (2304, 1041, 1280), (4097, 700, 768)])
+@pytest.mark.parametrize("shape", [(1100, 2300, 256), (1500, 1800, 512), (2304, 1041, 1280), (4097, 700, 768),
+                                   (100, 12800, 256)])
 @pytest.mark.parametrize("fa,fb", [(0, 0), (0, 1), (1, 0), (1, 1)])
 def test_gemm_fam16_large_tile_kernel(shape, fa, fb):
     """K % 256 == 0 with 40 or more 256 x 256 tiles runs the 16 x 16 x 128 pipelined kernel: 2 to
