@@ -686,10 +686,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias_pipe(const uint8_t *_
 //   step j computes with A_j (its fragments read one 16-row block ahead of the MFMAs) and B_j
 //   (whose fragments were read into registers during step j-1), while reading the fragments of
 //   B_{j+1} and, last, A_{j+1}'s first block.  B_j's slot is free once its fragments are in
-//   registers, so B runs a step further ahead than A: the loads of step j are A_{j+1} (into the
-//   slot A_{j-1} used) and B_{j+2} (into B_j's slot), 16 per wave, issued four after the previous
-//   step's barrier and four in each of the first three 16-row blocks; step j waits for them once,
-//   before its last block, with one barrier (which also frees A_j's and B_{j+1}'s slots).
+//   registers, so B runs a step further ahead than A: the loads of step j are B_{j+2} (into B_j's
+//   slot) and A_{j+1} (into the slot A_{j-1} used), 16 per wave, B's first, issued four after the
+//   previous step's barrier and four in each of the first three 16-row blocks; step j waits for
+//   them once, before its last block, with one barrier (which also frees A_j's and B_{j+1}'s
+//   slots).
 // Loads into LDS are buffer loads (per-tile descriptors, 32-bit lane offsets, the K step in the
 // scalar offset); a load index past the last K step is clamped to it (the extra loads at the end
 // refill free slots and are never read).  LDS rows are 128 bytes; 16-byte chunk c of row r sits
@@ -761,10 +762,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pipe16(const uint8_t *__re
 #define FP8DS_LD_B(SB_, j, i)                                                                              \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (__attribute__((address_space(3))) void *)((SB_) + ((i) * 4 + wave) * 1024), \
                                              16, vb[i], (uint32_t)(min((j), nk - 1) * kQK), 0, 0);
-    // loads n0 .. n1-1 of a step's 16, in the order A0 B0 A1 B1 ... (A step jA, B step jB)
+    // loads n0 .. n1-1 of a step's 16, B's eight first, then A's (A step jA, B step jB): each
+    // operand's loads issued as a group measured 2.5-4.3% faster on the two QKV shapes whose
+    // operands exceed the Infinity Cache than A and B alternating (A first: 1.7-3.1%)
 #define FP8DS_LDS(n0, n1, SA_, SB_, jA, jB)                                                                \
     _Pragma("unroll") for (int n = (n0); n < (n1); ++n) {                                                 \
-        if (n & 1) { FP8DS_LD_B(SB_, jB, n >> 1) } else { FP8DS_LD_A(SA_, jA, n >> 1) }                    \
+        if (n < 8) { FP8DS_LD_B(SB_, jB, n) } else { FP8DS_LD_A(SA_, jA, n - 8) }                          \
     }
 
     f32x4 acc[8][8];
