@@ -688,7 +688,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bias_pipe(const uint8_t *_
 //   B_{j+1} and, last, A_{j+1}'s first block.  B_j's slot is free once its fragments are in
 //   registers, so B runs a step further ahead than A: the loads of step j are B_{j+2} (into B_j's
 //   slot) and A_{j+1} (into the slot A_{j-1} used), 16 per wave, B's first, issued four after the
-//   previous step's barrier and four in each of the first three 16-row blocks; step j waits for
+//   previous step's barrier and three in each of the first four 16-row blocks; step j waits for
 //   them once, before its last block, with one barrier (which also frees A_j's and B_{j+1}'s
 //   slots).
 // Loads into LDS are buffer loads (per-tile descriptors, 32-bit lane offsets, the K step in the
@@ -816,16 +816,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pipe16(const uint8_t *__re
         __builtin_amdgcn_sched_barrier(0);                                                                \
     }
     // Step j: A_j in SA_CUR, A_{j+1} in SA_NXT, B_{j+1} in SB_NXT, B_j's slot SB_FREE, B_j's
-    // fragments in FBC.  Loads 4-15 of step j in blocks 0-2; wait + barrier; then block 7 reads the
-    // next step's A frag 0 and issues loads 0-3 of step j+1 (A_{j+2} into SA_CUR, B_{j+3} into
-    // SB_NXT), both slots freed by the barrier.
+    // fragments in FBC.  Loads 4-15 of step j in blocks 0-3 (three each); wait + barrier; then
+    // block 7 reads the next step's A frag 0 and issues loads 0-3 of step j+1 (the first four of
+    // B_{j+3}, into SB_NXT, which the barrier freed; A_{j+2} follows into SA_CUR in blocks 1-3).
 #define FP8DS_STEP16(j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN)                                         \
     {                                                                                                     \
         __builtin_amdgcn_sched_barrier(0);                                                                \
-        FP8DS_BLK(0, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, fa0, fa1, 4, 8)                         \
-        FP8DS_BLK(1, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, fa1, fa0, 8, 12)                        \
-        FP8DS_BLK(2, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, fa0, fa1, 12, 16)                       \
-        FP8DS_BLK(3, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, fa1, fa0, 16, 16)                       \
+        FP8DS_BLK(0, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, fa0, fa1, 4, 7)                         \
+        FP8DS_BLK(1, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, fa1, fa0, 7, 10)                        \
+        FP8DS_BLK(2, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, fa0, fa1, 10, 13)                       \
+        FP8DS_BLK(3, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, fa1, fa0, 13, 16)                       \
         FP8DS_BLK(4, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, fa0, fa1, 16, 16)                       \
         FP8DS_BLK(5, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, fa1, fa0, 16, 16)                       \
         FP8DS_BLK(6, j, SA_CUR, SA_NXT, SB_NXT, SB_FREE, FBC, FBN, fa0, fa1, 16, 16)                       \
