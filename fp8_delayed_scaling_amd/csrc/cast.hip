@@ -134,6 +134,30 @@ struct CtBatch {
     int64_t first1;
 };
 
+// Tile order.  With column tiles fastest, the ~512 blocks resident at once cover only about
+// 512 / tiles_c row tiles, so their transposed stores all fall in the same few 128-byte column
+// ranges of out_t, rows of out_t being `rows` bytes apart.  When that stride is a multiple of
+// 4 KB the stores crowd onto few HBM channels.  Such tensors (rows % 4096 == 0, at least two
+// groups of 32 row tiles, and at least 32 column tiles, i.e. fewer than 16 row tiles in flight
+// in the default order) take their tiles in groups of 32 row tiles, row tiles fastest inside a
+// group.  Measured against the default order on the same buffers: +1.5-3.4% at [8192, 12288]
+// and [12288, 12288], +6.8% at [16384, 12288], +9-11% for the [8192, 18432] E5M2 gradient;
+// grouping [18432, 12288] (stride not a multiple of 4 KB) was 3-9% slower, [4096, 12288] (one
+// group) 2.8% slower and [8192, 4096] (16 column tiles) 5% slower, so those keep the default.
+constexpr int kRowGroup = 32;
+__device__ __forceinline__ void ct_tile_of(int64_t block, int64_t rows, int64_t tiles_c, int64_t &tile_r,
+                                           int64_t &tile_c) {
+    if (rows % 4096 == 0 && rows >= 2 * kRowGroup * kTile && tiles_c >= 32) {
+        // rows is a multiple of 32 tiles, so every group is full
+        const int64_t per = kRowGroup * tiles_c, g = block / per, local = block - g * per;
+        tile_r = g * kRowGroup + local % kRowGroup;
+        tile_c = local / kRowGroup;
+    } else {
+        tile_r = block / tiles_c;
+        tile_c = block - tile_r * tiles_c;
+    }
+}
+
 template <int FMT, bool VEC, bool DBIAS>
 __global__ __launch_bounds__(kCtThreads) void k_cast_transpose(const CtBatch batch, float *__restrict__ partial) {
     __shared__ __align__(16) uint8_t tT[kTileC * kTile];
@@ -152,7 +176,8 @@ __global__ __launch_bounds__(kCtThreads) void k_cast_transpose(const CtBatch bat
     const int rb = t >> 5, cb = t & 31;
     const int64_t block = (int64_t)blockIdx.x - (second ? batch.first1 : 0);
     const int64_t tiles_c = (cols + kTileC - 1) / kTileC;
-    const int64_t tile_r = block / tiles_c, tile_c = block - tile_r * tiles_c;
+    int64_t tile_r, tile_c;
+    ct_tile_of(block, rows, tiles_c, tile_r, tile_c);
     const int64_t r0 = tile_r * kTile;
     const int64_t c0 = tile_c * kTileC;
     const int64_t row = r0 + rb * 8;   // first row of the micro-tile

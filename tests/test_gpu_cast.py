@@ -89,6 +89,20 @@ def test_cast_transpose_parity(fmt, shape):
         assert f32_bits(amax) == f32_bits(ramax) and f32_bits(sinv) == f32_bits(rsinv)
 
 
+@pytest.mark.parametrize("fmt,shape", [(F.E4M3, (8192, 8200)), (F.E5M2, (8192, 8193)), (F.E4M3, (12288, 8448))])
+def test_cast_transpose_grouped_tile_order(fmt, shape):
+    """Tensors whose rows are a multiple of 4096 (at least 8192) with at least 32 column tiles
+    take their tiles in groups of 32 row tiles: every tile is covered once, with a ragged column
+    tail on the 16-byte path (8200 columns) and on the element-wise path (8193 columns)."""
+    print(f"cast_transpose grouped order fmt={fmt} shape={shape}", flush=True)
+    xh = S.outlier_bf16(S.seed_for(13, 11 + shape[1] % 5), shape, 1.0)
+    q, qt, amax, sinv = _run_ct(xh, 21.0, fmt)
+    rq, rqt, ramax, rsinv = oracle.cast_transpose(xh, 21.0, fmt)
+    assert np.array_equal(q, rq)
+    assert np.array_equal(qt, rqt)
+    assert f32_bits(amax) == f32_bits(ramax) and f32_bits(sinv) == f32_bits(rsinv)
+
+
 def test_cast_transpose_noop_flag():
     xh = S.normal_bf16(S.seed_for(14, 0), (256, 384), 1.0)
     q, qt, amax, sinv = _run_ct(xh, 1.0, F.E4M3, noop=scalar(1.0))
@@ -158,7 +172,8 @@ def _dbias_bound(dyh):
     return 1e-5 * np.abs(S.bf16_bits_to_f64(dyh)).sum(axis=0) + 1e-30
 
 
-@pytest.mark.parametrize("shape", [(1, 1), (3, 5), (130, 264), (144, 264), (257, 383), (8192, 4096), (17297, 136)])
+@pytest.mark.parametrize("shape", [(1, 1), (3, 5), (130, 264), (144, 264), (257, 383), (8192, 4096), (17297, 136),
+                                   (8192, 8200)])
 def test_dbias_cast_transpose_parity(shape):
     print(f"dbias_cast_transpose {shape}", flush=True)
     R, C = shape
