@@ -120,35 +120,56 @@ def _check(status: int):
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
 
 
-def _want(t, dtypes, name, contiguous=True):
+_F32 = (torch.float32,)
+_U8 = (torch.uint8,)
+
+
+def _want(t, dtypes, name, contiguous=True, shape=None, min_numel=None, required=False):
+    """Check a tensor argument before its pointer goes to the library, which cannot see sizes:
+    dtype, density, and the exact ``shape`` or at least ``min_numel`` elements.  A plain int is
+    a raw device pointer and is passed through unchecked."""
     if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return
+    if isinstance(t, int):
         return
     if t.dtype not in dtypes:
         raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
     if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} must hold at least {min_numel} elements, got {t.numel()}")
+
+
+def _scalars(**kw):
+    """float32 device scalars (scale, inverse scale, amax slot, noop flag): one element each."""
+    for name, t in kw.items():
+        _want(t, _F32, name, min_numel=1)
 
 
 # ----------------------------------------------------------------------------- entry points
 
 def fp8_cast_amax(x, scale, fmt, out, scale_inv_out=None, amax_slot=None, noop=None, stream=None):
     """Cast bfloat16 ``x`` to FP8 codes ``out`` with amax capture (see include/fp8ds.h)."""
-    _want(x, _BF16, "x")
-    _want(out, (torch.uint8,), "out")
+    _want(x, _BF16, "x", required=True)
+    _want(out, _U8, "out", required=True)
     if out.numel() != x.numel():
         raise ValueError("out must have x's number of elements")
+    _scalars(scale=scale, scale_inv_out=scale_inv_out, amax_slot=amax_slot, noop=noop)
     _check(lib().fp8_cast_amax(_ptr(x), x.numel(), _ptr(scale), int(fmt), _ptr(out), _ptr(scale_inv_out),
                                _ptr(amax_slot), _ptr(noop), _stream(stream)))
 
 
 def fp8_cast_transpose(x, scale, fmt, out, out_t, scale_inv_out=None, amax_slot=None, noop=None, stream=None):
     """Cast a 2-D bfloat16 ``x`` [R, C] to ``out`` [R, C] and its transpose ``out_t`` [C, R]."""
-    _want(x, _BF16, "x")
-    _want(out, (torch.uint8,), "out")
-    _want(out_t, (torch.uint8,), "out_t")
+    _want(x, _BF16, "x", required=True)
     R, C = x.shape
-    if tuple(out.shape) != (R, C) or tuple(out_t.shape) != (C, R):
-        raise ValueError("out must be [R, C] and out_t [C, R]")
+    _want(out, _U8, "out", shape=(R, C), required=True)
+    _want(out_t, _U8, "out_t", shape=(C, R), required=True)
+    _scalars(scale=scale, scale_inv_out=scale_inv_out, amax_slot=amax_slot, noop=noop)
     _check(lib().fp8_cast_transpose(_ptr(x), R, C, _ptr(scale), int(fmt), _ptr(out), _ptr(out_t),
                                     _ptr(scale_inv_out), _ptr(amax_slot), _ptr(noop), _stream(stream)))
 
@@ -160,11 +181,14 @@ def fp8_dbias_workspace_bytes(rows: int, cols: int) -> int:
 def fp8_dbias_cast_transpose(dy, scale, fmt, out, out_t, dbias, workspace, scale_inv_out=None, amax_slot=None,
                              stream=None):
     """dbias = column sums of ``dy`` plus its cast+transpose (see include/fp8ds.h)."""
-    _want(dy, _BF16, "dy")
-    _want(dbias, (torch.float32,), "dbias")
+    _want(dy, _BF16, "dy", required=True)
     R, C = dy.shape
-    if out is not None and (tuple(out.shape) != (R, C) or tuple(out_t.shape) != (C, R)):
-        raise ValueError("out must be [R, C] and out_t [C, R]")
+    _want(dbias, _F32, "dbias", shape=(C,), required=True)
+    _want(out, _U8, "out", shape=(R, C))
+    _want(out_t, _U8, "out_t", shape=(C, R))
+    if isinstance(workspace, torch.Tensor) and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _scalars(scale=scale, scale_inv_out=scale_inv_out, amax_slot=amax_slot)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().fp8_dbias_cast_transpose(_ptr(dy), R, C, _ptr(scale), int(fmt), _ptr(out), _ptr(out_t),
                                           _ptr(scale_inv_out), _ptr(amax_slot), _ptr(dbias), _ptr(workspace),
@@ -173,11 +197,13 @@ def fp8_dbias_cast_transpose(dy, scale, fmt, out, out_t, dbias, workspace, scale
 
 def fp8_scale_update(amax_history, scale, scale_inv, fmts: Sequence[int], margin: int = 0, stream=None):
     """One delayed-scaling step for the T tensors of ``amax_history`` [L, T]."""
-    _want(amax_history, (torch.float32,), "amax_history")
+    _want(amax_history, _F32, "amax_history", required=True)
     L, T = amax_history.shape
-    f = (ctypes.c_int32 * T)(*[int(v) for v in fmts])
+    _want(scale, _F32, "scale", min_numel=T, required=True)
+    _want(scale_inv, _F32, "scale_inv", min_numel=T, required=True)
     if len(fmts) != T:
         raise ValueError("one format per tensor")
+    f = (ctypes.c_int32 * T)(*[int(v) for v in fmts])
     _check(lib().fp8_scale_update(_ptr(amax_history), L, T, _ptr(scale), _ptr(scale_inv),
                                   ctypes.cast(f, ctypes.c_void_p), int(margin), _stream(stream)))
 
@@ -191,18 +217,19 @@ def _out_dtype(D):
 
 
 def _gemm_args(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D):
-    _want(A, (torch.uint8,), "A", contiguous=False)
-    _want(B, (torch.uint8,), "B", contiguous=False)
-    _want(bias, _BF16, "bias")
+    _want(A, _U8, "A", contiguous=False, required=True)
+    _want(B, _U8, "B", contiguous=False, required=True)
     M, K = A.shape
     N, K2 = B.shape
     if K != K2:
         raise ValueError("A and B must share K")
+    _want(bias, _BF16, "bias", shape=(N,))
     if tuple(D.shape) != (M, N):
         raise ValueError("D must be [M, N]")
     for t, nm in ((A, "A"), (B, "B"), (D, "D")):
         if t.numel() and t.stride(1) != 1:
             raise ValueError(f"{nm} rows must be contiguous")
+    _scalars(a_scale_inv=a_scale_inv, b_scale_inv=b_scale_inv)
     return (_ptr(A), int(fa), _ptr(a_scale_inv), A.stride(0), _ptr(B), int(fb), _ptr(b_scale_inv), B.stride(0),
             _ptr(bias), _ptr(D), D.stride(0), _out_dtype(D), M, N, K)
 
@@ -216,14 +243,16 @@ def fp8_gemm_bias_fp8(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D, d_fmt, d_
                       d_amax_slot=None, stream=None):
     """FP8-output GEMM: D = codes of ((A B^T) * a_scale_inv * b_scale_inv + bias) * d_scale, with the
     output's amax folded into ``d_amax_slot`` and 1/d_scale written to ``d_scale_inv_out``."""
-    _want(D, (torch.uint8,), "D", contiguous=False)
-    _want(A, (torch.uint8,), "A", contiguous=False)
-    _want(B, (torch.uint8,), "B", contiguous=False)
-    _want(bias, _BF16, "bias")
+    _want(D, _U8, "D", contiguous=False, required=True)
+    _want(A, _U8, "A", contiguous=False, required=True)
+    _want(B, _U8, "B", contiguous=False, required=True)
     M, K = A.shape
     N, K2 = B.shape
     if K != K2:
         raise ValueError("A and B must share K")
+    _want(bias, _BF16, "bias", shape=(N,))
+    _scalars(a_scale_inv=a_scale_inv, b_scale_inv=b_scale_inv, d_scale=d_scale, d_scale_inv_out=d_scale_inv_out,
+             d_amax_slot=d_amax_slot)
     if tuple(D.shape) != (M, N):
         raise ValueError("D must be [M, N]")
     for t, nm in ((A, "A"), (B, "B"), (D, "D")):
@@ -237,11 +266,10 @@ def fp8_gemm_bias_fp8(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D, d_fmt, d_
 
 def fp8_transpose(x8, out_t, noop=None, stream=None):
     """Transpose cache of an existing FP8 tensor: out_t [C, R] = x8 [R, C]^T (codes copied)."""
-    _want(x8, (torch.uint8,), "x8")
-    _want(out_t, (torch.uint8,), "out_t")
+    _want(x8, _U8, "x8", required=True)
     R, C = x8.shape
-    if tuple(out_t.shape) != (C, R):
-        raise ValueError("out_t must be [C, R]")
+    _want(out_t, _U8, "out_t", shape=(C, R), required=True)
+    _scalars(noop=noop)
     _check(lib().fp8_transpose(_ptr(x8), R, C, _ptr(out_t), _ptr(noop), _stream(stream)))
 
 
@@ -261,13 +289,20 @@ def fp8_gemm_bias_chunked(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D, n_chu
 def fp8_linear_fwd(x, w, bias, x_scale, x_amax, x8, x8_t, x_scale_inv, w_scale, w_amax, w8, w8_t, w_scale_inv,
                    w_noop, y, stream=None):
     """Forward of the FP8 linear layer: casts of x and W, then y = x8 W8^T + bias."""
-    _want(x, _BF16, "x")
-    _want(w, _BF16, "w")
-    _want(y, (torch.bfloat16,), "y")
+    _want(x, _BF16, "x", required=True)
+    _want(w, _BF16, "w", required=True)
     M, K = x.shape
     N, K2 = w.shape
-    if K != K2 or tuple(y.shape) != (M, N):
-        raise ValueError("x [M, K], w [N, K], y [M, N]")
+    if K != K2:
+        raise ValueError("x [M, K] and w [N, K] must share K")
+    _want(y, (torch.bfloat16,), "y", shape=(M, N), required=True)
+    _want(bias, _BF16, "bias", shape=(N,))
+    _want(x8, _U8, "x8", shape=(M, K), required=True)
+    _want(x8_t, _U8, "x8_t", shape=(K, M))
+    _want(w8, _U8, "w8", shape=(N, K), required=True)
+    _want(w8_t, _U8, "w8_t", shape=(K, N), required=True)
+    _scalars(x_scale=x_scale, x_amax=x_amax, x_scale_inv=x_scale_inv, w_scale=w_scale, w_amax=w_amax,
+             w_scale_inv=w_scale_inv, w_noop=w_noop)
     _check(lib().fp8_linear_fwd(_ptr(x), _ptr(w), _ptr(bias), M, N, K, _ptr(x_scale), _ptr(x_amax), _ptr(x8),
                                 _ptr(x8_t), _ptr(x_scale_inv), _ptr(w_scale), _ptr(w_amax), _ptr(w8), _ptr(w8_t),
                                 _ptr(w_scale_inv), _ptr(w_noop), _ptr(y), _stream(stream)))
@@ -276,8 +311,18 @@ def fp8_linear_fwd(x, w, bias, x_scale, x_amax, x8, x8_t, x_scale_inv, w_scale, 
 def fp8_linear_bwd(dy, K, dy_scale, dy_amax, dy8, dy8_t, dy_scale_inv, dbias, workspace, x8_t, x_scale_inv, w8_t,
                    w_scale_inv, dx, dw, stream=None):
     """Backward of the FP8 linear layer: dbias + cast+transpose of dy, dgrad and wgrad GEMMs."""
-    _want(dy, _BF16, "dy")
+    _want(dy, _BF16, "dy", required=True)
     M, N = dy.shape
+    K = int(K)
+    _want(dy8, _U8, "dy8", shape=(M, N), required=True)
+    _want(dy8_t, _U8, "dy8_t", shape=(N, M), required=True)
+    _want(dbias, _F32, "dbias", shape=(N,))
+    _want(x8_t, _U8, "x8_t", shape=(K, M), required=True)
+    _want(w8_t, _U8, "w8_t", shape=(K, N), required=True)
+    _want(dx, (torch.bfloat16,), "dx", shape=(M, K), required=True)
+    _want(dw, (torch.bfloat16, torch.float32), "dw", shape=(N, K), required=True)
+    _scalars(dy_scale=dy_scale, dy_amax=dy_amax, dy_scale_inv=dy_scale_inv, x_scale_inv=x_scale_inv,
+             w_scale_inv=w_scale_inv)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().fp8_linear_bwd(_ptr(dy), M, N, int(K), _ptr(dy_scale), _ptr(dy_amax), _ptr(dy8), _ptr(dy8_t),
                                 _ptr(dy_scale_inv), _ptr(dbias), _ptr(workspace), ws_bytes, _ptr(x8_t),

@@ -24,13 +24,12 @@ __global__ __launch_bounds__(256) void k_scale_update(float *__restrict__ hist, 
                                                       float *__restrict__ scale, float *__restrict__ scale_inv,
                                                       FmtMask fm, float pow2_neg_margin) {
     __shared__ float red[4];
-    __shared__ int nanflag;
+    __shared__ int nanw[4];   // per wave: any NaN in the rows it read (written once, no init)
     __shared__ __align__(16) float col[kSuLdsRows];
     const int64_t t = blockIdx.x;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool staged = L <= kSuLdsRows;   // uniform
-    if (tid == 0) nanflag = 0;
 
     // pass 1: max over the window (all L rows), NaN tracked on its own
     float a = 0.f, row0, prev_scale;
@@ -63,20 +62,24 @@ __global__ __launch_bounds__(256) void k_scale_update(float *__restrict__ hist, 
         }
         row0 = hist[t];   // old row 0, read before any write below
     }
-    if (nan) nanflag = 1;
+    const bool wave_nan = __ballot(nan) != 0;   // every lane of the wave takes part
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
-    if ((tid & 63) == 0) red[tid >> 6] = a;
+    if ((tid & 63) == 0) {
+        red[tid >> 6] = a;
+        nanw[tid >> 6] = wave_nan ? 1 : 0;
+    }
     __syncthreads();
 
     if (tid == 0) {
         float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-        if (nanflag) amax = __uint_as_float(0x7FC00000u);
+        if (nanw[0] | nanw[1] | nanw[2] | nanw[3]) amax = __uint_as_float(0x7FC00000u);
         const bool e5 = (fm.bits[t >> 5] >> (t & 31)) & 1u;
         const float fmax = e5 ? FmtTraits<kE5M2>::kMax : FmtTraits<kE4M3>::kMax;
         float s = (fmax / amax) * pow2_neg_margin;
-        const bool bad = !(amax > 0.f) || !(amax < __uint_as_float(0x7F800000u)) ||
-                         !(fabsf(s) < __uint_as_float(0x7F800000u)) || s == 0.f;
+        // a zero scale, or one below 2^-128, has an inverse that overflows float32
+        const float inf = __uint_as_float(0x7F800000u);
+        const bool bad = !(amax > 0.f) || !(amax < inf) || !(fabsf(s) < inf) || !(fabsf(1.0f / s) < inf);
         if (bad) s = prev_scale;
         scale[t] = s;
         scale_inv[t] = 1.0f / s;

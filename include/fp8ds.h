@@ -137,7 +137,8 @@ int fp8_dbias_cast_transpose(const uint16_t *dy, int64_t rows, int64_t cols, con
  * For every tensor t:
  *   a = max over rows 0..L-1 of amax_history[.][t]    (NaN dominates)
  *   s = (fp8_max(fmts[t]) / a) * 2^-margin            float32
- *   if a == 0, a is not finite, s is not finite or s == 0: s = scale[t] (previous kept)
+ *   if a == 0, a is not finite, s is not finite or 1.0f / s is not finite (s == 0, or s
+ *   below 2^-128): s = scale[t] (previous kept)
  *   scale[t] = s;  scale_inv[t] = 1.0f / s
  *   history: row i takes row i+1 (i < L-1), row L-1 takes the old row 0, row 0 becomes 0.
  * The FP8 tensors' private inverse scales are NOT touched: they change only when a tensor is

@@ -258,7 +258,8 @@ float orc_scale_inv(float scale) { return 1.0f / scale; }
  *   a      = max over the L rows of hist[.][t]          (the current amax and L-1 earlier ones)
  *   s      = (fp8_max / a) * 2^-margin                   (float32: one division, one exact
  *                                                         power-of-two product)
- *   guard  : keep the previous scale if a == 0, a is not finite, s is not finite, or s == 0
+ *   guard  : keep the previous scale if a == 0, a is not finite, s is not finite, or 1/s is
+ *            not finite (s == 0, or s so small that its float32 inverse overflows)
  *   scale[t] = s; scale_inv[t] = 1/s (float32)
  *   history: every row moves one place towards row 0 (row i takes row i+1), row L-1 takes
  *            the old row 0 (the amax just used), and row 0 is cleared for the next iteration.
@@ -279,7 +280,7 @@ void orc_scale_update(float *hist, int64_t L, int64_t T, float *scale, float *sc
             else if (h > a) a = h;
         }
         s = (fmax / a) * p;
-        if (a == 0.0f || !isfinite(a) || !isfinite(s) || s == 0.0f) s = scale[t];
+        if (a == 0.0f || !isfinite(a) || !isfinite(s) || !isfinite(1.0f / s)) s = scale[t];
         scale[t] = s;
         scale_inv[t] = 1.0f / s;
         row0 = old[t];

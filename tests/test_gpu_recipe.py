@@ -89,6 +89,45 @@ def test_scale_update_guard_cases_and_many_tensors(L, T):
             assert _same(g, r), margin
 
 
+@pytest.mark.parametrize("L", [300, 9000])
+def test_scale_update_nan_read_by_every_wave(L):
+    """A NaN in any row of the window keeps the previous scale, whichever of the block's four
+    waves reads it: thread i reads rows i, i + 256, ..., so row r goes to wave (r % 256) // 64.
+    Tensor t holds one NaN in a row of wave t (the last tensor none), on the LDS-staged path
+    (L = 300) and on the chunked path (L = 9000)."""
+    T = 6
+    nan_rows = [2, 70, 130, 200, L - 50]          # waves 0, 1, 2, 3 and a late row
+    h = S.log_uniform_f32(S.seed_for(6, 77), L * T, 1e-3, 1e3).reshape(L, T)
+    for t, r in enumerate(nan_rows):
+        h[r, t] = np.nan
+    s = S.log_uniform_f32(S.seed_for(6, 78), T, 0.5, 2.0)
+    si = (1 / s).astype(np.float32)
+    fm = [F.E4M3, F.E5M2, F.E4M3, F.E5M2, F.E4M3, F.E4M3]
+    got = _update(h, s, si, fm, 0)
+    ref = oracle.scale_update(h, s, si, fm, 0)
+    for g, r in zip(got, ref):
+        assert _same(g, r)
+    assert _same(got[1][:5], s[:5]) and not _same(got[1][5:], s[5:])   # NaN windows kept their scale
+
+
+@pytest.mark.parametrize("margin", [126, 125])
+def test_scale_update_tiny_scale_guard(margin):
+    """Amaxes at and around the point where (fp8_max / a) * 2^-margin, or its inverse, leaves
+    the float32 range: 448, 896 (scale 2^-127, inverse finite), 1792 (inverse overflows), 1e6
+    (subnormal scale), FLT_MAX (scale 0), on the GPU against the oracle."""
+    am = np.array([448.0, 896.0, 1792.0, 1e6, 3.4028235e38, 57344.0], np.float32)
+    T = am.size
+    h = np.zeros((4, T), np.float32)
+    h[1] = am
+    s = np.full(T, 3.0, np.float32)
+    si = (1 / s).astype(np.float32)
+    fm = [F.E4M3] * 5 + [F.E5M2]
+    got = _update(h, s, si, fm, margin)
+    ref = oracle.scale_update(h, s, si, fm, margin)
+    for g, r in zip(got, ref):
+        assert _same(g, r)
+
+
 def test_scale_update_rejects_bad_arguments():
     hd = torch.zeros((4, 2), device=DEV)
     sd = torch.ones(2, device=DEV)

@@ -236,6 +236,19 @@ def test_scale_update_golden():
         assert _bits(si[0]) == int(wsi, 16), (abits, margin, hex(_bits(si[0])))
 
 
+def test_scale_update_window_golden():
+    """Hand-worked whole windows: a NaN in any row (not only row 0) keeps the previous scale,
+    the max may sit in any row, and the roll moves every row one place towards row 0."""
+    for fmt, margin, prev, hist, ws, wsi, rolled, *_ in _rows("scale_update_window.txt"):
+        h = np.array([int(v, 16) for v in hist.split(",")], np.uint32).view(np.float32).reshape(-1, 1)
+        s0 = _f32(prev)
+        h2, s, si = oracle.scale_update(h, s0, 1.0 / s0, [FMT[fmt]], int(margin))
+        assert _bits(s[0]) == int(ws, 16), (hist, hex(_bits(s[0])))
+        assert _bits(si[0]) == int(wsi, 16), (hist, hex(_bits(si[0])))
+        want = [int(v, 16) for v in rolled.split(",")]
+        assert [int(b) for b in np.asarray(h2, np.float32).reshape(-1).view(np.uint32)] == want, hist
+
+
 def test_scale_update_l1_reduces_to_fp8max_over_amax():
     a = S.log_uniform_f32(77, 200, 1e-3, 1e3)
     for fmt in (oracle.E4M3, oracle.E5M2):
