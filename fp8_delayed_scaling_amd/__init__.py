@@ -22,7 +22,7 @@ __all__ = [
     "E4M3", "E5M2", "OUT_BF16", "OUT_FP32", "Fp8dsError", "lib", "library_path",
     "fp8ds_status_string", "fp8ds_version",
     "fp8_cast_amax", "fp8_cast_transpose", "fp8_dbias_workspace_bytes", "fp8_dbias_cast_transpose",
-    "fp8_scale_update", "fp8_gemm_bias", "fp8_gemm_bias_chunked", "fp8_gemm_bias_fp8", "fp8_transpose",
+    "fp8_dbias_cast_transpose_noalloc", "fp8_scale_update", "fp8_gemm_bias", "fp8_gemm_bias_chunked", "fp8_gemm_bias_fp8", "fp8_transpose",
     "fp8_linear_fwd", "fp8_linear_bwd",
 ]
 
@@ -57,6 +57,7 @@ _SIGS = {
     "fp8_cast_transpose": ([P, I64, I64, P, INT, P, P, P, P, P, P], INT),
     "fp8_dbias_workspace_bytes": ([I64, I64], SZ),
     "fp8_dbias_cast_transpose": ([P, I64, I64, P, INT, P, P, P, P, P, P, SZ, P], INT),
+    "fp8_dbias_cast_transpose_noalloc": ([P, I64, I64, P, INT, P, P, P, P, P, P], INT),
     "fp8_scale_update": ([P, I64, I64, P, P, P, I32, P], INT),
     "fp8_gemm_bias": ([P, INT, P, I64, P, INT, P, I64, P, P, I64, INT, I64, I64, I64, P], INT),
     "fp8_gemm_bias_chunked": ([P, INT, P, I64, P, INT, P, I64, P, P, I64, INT, I64, I64, I64, INT, P, P], INT),
@@ -193,6 +194,21 @@ def fp8_dbias_cast_transpose(dy, scale, fmt, out, out_t, dbias, workspace, scale
     _check(lib().fp8_dbias_cast_transpose(_ptr(dy), R, C, _ptr(scale), int(fmt), _ptr(out), _ptr(out_t),
                                           _ptr(scale_inv_out), _ptr(amax_slot), _ptr(dbias), _ptr(workspace),
                                           ws_bytes, _stream(stream)))
+
+
+def fp8_dbias_cast_transpose_noalloc(dy, scale, fmt, out, out_t, dbias, scale_inv_out=None, amax_slot=None,
+                                     stream=None):
+    """fp8_dbias_cast_transpose without a workspace: the partial sums go to the library's static
+    per-GPU scratch (no allocation; calls overlapping on one GPU race; see include/fp8ds.h)."""
+    _want(dy, _BF16, "dy", required=True)
+    R, C = dy.shape
+    _want(dbias, _F32, "dbias", shape=(C,), required=True)
+    _want(out, _U8, "out", shape=(R, C))
+    _want(out_t, _U8, "out_t", shape=(C, R))
+    _scalars(scale=scale, scale_inv_out=scale_inv_out, amax_slot=amax_slot)
+    _check(lib().fp8_dbias_cast_transpose_noalloc(_ptr(dy), R, C, _ptr(scale), int(fmt), _ptr(out), _ptr(out_t),
+                                                  _ptr(scale_inv_out), _ptr(amax_slot), _ptr(dbias),
+                                                  _stream(stream)))
 
 
 def fp8_scale_update(amax_history, scale, scale_inv, fmts: Sequence[int], margin: int = 0, stream=None):

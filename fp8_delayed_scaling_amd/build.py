@@ -11,7 +11,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libfp8ds.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["cast.hip", "transpose.hip", "scale_update.hip", "gemm.hip", "api.cpp"]
+SOURCES = ["cast.hip", "transpose.hip", "scale_update.hip", "gemm.hip", "api.cpp", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # No fast-math and no denormal flushing (the casts must round float32 subnormals exactly);

@@ -107,6 +107,7 @@ const char *fp8ds_status_string(int status) {
         case FP8DS_ERR_WORKSPACE: return "FP8DS_ERR_WORKSPACE: workspace missing or too small";
         case FP8DS_ERR_HIP: return "FP8DS_ERR_HIP: the HIP runtime reported an error";
         case FP8DS_ERR_ARG: return "FP8DS_ERR_ARG: argument out of range";
+        case FP8DS_ERR_SCRATCH: return "FP8DS_ERR_SCRATCH: problem larger than the library's static scratch";
         default: return "FP8DS: unknown status";
     }
 }

@@ -56,7 +56,8 @@ typedef enum {
     FP8DS_ERR_FORMAT = -4,    /* unknown fp8ds_format / fp8ds_out_dtype            */
     FP8DS_ERR_WORKSPACE = -5, /* workspace missing or smaller than required        */
     FP8DS_ERR_HIP = -6,       /* the HIP runtime reported an error                 */
-    FP8DS_ERR_ARG = -7        /* another argument is out of its documented range   */
+    FP8DS_ERR_ARG = -7,       /* another argument is out of its documented range   */
+    FP8DS_ERR_SCRATCH = -8    /* the problem needs more than the static scratch    */
 } fp8ds_status;
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -126,6 +127,24 @@ int fp8_dbias_cast_transpose(const uint16_t *dy, int64_t rows, int64_t cols, con
                              int fmt, uint8_t *out, uint8_t *out_t, float *scale_inv_out,
                              float *amax_slot, float *dbias, void *workspace,
                              size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fp8_dbias_cast_transpose_noalloc -- fp8_dbias_cast_transpose for callers that cannot
+ * allocate device memory or pass a workspace (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and kernels, minus the
+ * workspace: the partial column sums go to a static device array of
+ * FP8DS_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on until the process
+ * ends.  Calls nothing that allocates.  Limit: fp8_dbias_workspace_bytes(rows, cols) <=
+ * FP8DS_NOALLOC_SCRATCH_BYTES (8 MiB: e.g. [8192, 16384] needs 4 MiB, [8192, 32768] 8 MiB),
+ * else FP8DS_ERR_SCRATCH and nothing is launched.  All calls on one GPU share its array and
+ * each call overwrites it, so calls that overlap in time on one GPU (on two streams, or from
+ * two host threads) race: serialise them.
+ */
+#define FP8DS_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int fp8_dbias_cast_transpose_noalloc(const uint16_t *dy, int64_t rows, int64_t cols,
+                                     const float *scale, int fmt, uint8_t *out, uint8_t *out_t,
+                                     float *scale_inv_out, float *amax_slot, float *dbias,
+                                     hipStream_t stream);
 
 /*
  * fp8_scale_update -- one delayed-scaling step for T tensors in one launch ([WS] Motivations,

@@ -21,7 +21,8 @@ def test_header_declares_the_hot_path():
     names = _declared()
     for n in ("fp8_cast_amax", "fp8_cast_transpose", "fp8_dbias_cast_transpose", "fp8_dbias_workspace_bytes",
               "fp8_scale_update", "fp8_gemm_bias", "fp8_gemm_bias_chunked", "fp8_gemm_bias_fp8", "fp8_transpose",
-              "fp8_linear_fwd", "fp8_linear_bwd", "fp8ds_status_string", "fp8ds_version"):
+              "fp8_linear_fwd", "fp8_linear_bwd", "fp8ds_status_string", "fp8ds_version",
+              "fp8_dbias_cast_transpose_noalloc"):
         assert n in names, n
 
 
@@ -33,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         s = F.fp8ds_status_string(code)
         assert s.startswith("FP8DS")
     assert "unknown" in F.fp8ds_status_string(-99)
@@ -62,6 +63,18 @@ def test_dbias_validation():
     assert L.fp8_dbias_cast_transpose(A16, 300, 100, A16, 1, A16, A16, None, None, A16, None, 0, None) == -5
     assert L.fp8_dbias_cast_transpose(A16, 300, 100, A16, 1, A16, A16, None, None, A16, A16, need - 4, None) == -5
     assert L.fp8_dbias_cast_transpose(A16, 300, 100, A16, 1, A16, A16, None, None, None, A16, need, None) == -1
+
+
+def test_dbias_noalloc_rejects_sizes_beyond_its_scratch():
+    L = F.lib()
+    f = L.fp8_dbias_cast_transpose_noalloc
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    # 64 row blocks x 40000 columns x 4 bytes = 10.24 MB of partials > 8 MiB: rejected, nothing launched
+    assert F.fp8_dbias_workspace_bytes(8192, 40000) > 8 << 20
+    assert f(A16, 8192, 40000, A16, 1, A16, A16, None, None, A16, None) == -8
+    assert f(A16, -1, 100, A16, 1, A16, A16, None, None, A16, None) == -2
 
 
 def test_scale_update_validation():
