@@ -21,10 +21,14 @@ Also reported (own timings, HIP events on the launch stream):
   * the FP8-output GEMM (E5M2 output, own scale, amax capture) at the dgrad shape, against the
     bfloat16-output GEMM on the same operands;
   * a plain 1 GiB device copy, cold: the box's own streaming ceiling for the cast kernels;
-  * for context only, the vendor library's FP8 GEMM (hipBLASLt via torch._scaled_mm) beside this
-    library's GEMM on the same forward-shape operands;
-  * the CPU oracle on a bounded sample of the same step, one thread and all host cores
-    (baseline only).
+  * the CPU oracle, one thread and threaded over row blocks on the host cores (baseline only):
+    the cast family at full size (small layer, cast+transpose sweep, backward prep) and a
+    bounded sample of the step.
+"Cold" cast timings rotate over enough buffer sets that every launch reads input and writes
+output last touched more than 1 GiB of traffic earlier (beyond the 256 MB Infinity Cache and
+the L2s), with back-to-back launches between one pair of events, so the average is the
+kernel's own duration (comparable with a profiler's kernel trace).
+`--casts-only` runs only the cast-family timings (for an isolated profiler trace).
 """
 from __future__ import annotations
 
@@ -43,6 +47,8 @@ FP8_PEAK = 5.0e15          # FLOP/s, MI355X dense FP8 MFMA
 
 M, K, N = 8192, 12288, 18432
 HIST_L = 1024
+CT_SHAPES = [(1024, 1024), (4096, 4096), (8192, 12288)]   # cast+transpose sweep
+PREP_SHAPE = (8192, 4096)                                 # backward prep: dy
 
 
 def parse():
@@ -55,42 +61,10 @@ def parse():
     p.add_argument("--traffic-probe", action="store_true",
                    help="only launch one plain 1 GiB device copy and one forward GEMM (for rocprofv3 --pmc "
                         "FETCH_SIZE / WRITE_SIZE passes: the copy calibrates the counters)")
-    p.add_argument("--mfma-probe", action="store_true",
-                   help="only launch the forward GEMM three times and the vendor library's FP8 GEMM "
-                        "(torch._scaled_mm) three times on the same operands (for rocprofv3 --pmc passes "
-                        "comparing matrix-core busy cycles, wait cycles and total cycles)")
+    p.add_argument("--casts-only", action="store_true",
+                   help="only the cold cast-family timings (cast+transpose sweep, cast+amax, backward prep), "
+                        "printed as one JSON line (for an isolated rocprofv3 kernel trace)")
     return p.parse_args()
-
-
-def mfma_probe():
-    """The forward QKV GEMM of this library and torch._scaled_mm (hipBLASLt) on the same FP8
-    operands -- x ~ N(0,1) and W ~ N(0,0.02) cast to E4M3 by this library's cast -- three launches
-    each, synchronised one by one, nothing else on the GPU."""
-    import torch
-
-    import fp8_delayed_scaling_amd as F
-
-    F.lib()
-    dev = torch.device("cuda:0")
-    g = torch.Generator(device=dev).manual_seed(13)
-    x = torch.randn((M, K), device=dev, generator=g).to(torch.bfloat16)
-    w = (torch.randn((N, K), device=dev, generator=g) * 0.02).to(torch.bfloat16)
-    x8, w8 = torch.empty((M, K), dtype=torch.uint8, device=dev), torch.empty((N, K), dtype=torch.uint8, device=dev)
-    sx, sw = torch.full((1,), 60.0, device=dev), torch.full((1,), 2000.0, device=dev)
-    six, siw = torch.zeros(1, device=dev), torch.zeros(1, device=dev)
-    F.fp8_cast_amax(x, sx, F.E4M3, x8.view(-1), six, None)
-    F.fp8_cast_amax(w, sw, F.E4M3, w8.view(-1), siw, None)
-    del x, w
-    y = torch.empty((M, N), device=dev, dtype=torch.bfloat16)
-    a8, b8 = x8.view(torch.float8_e4m3fn), w8.view(torch.float8_e4m3fn)
-    torch.cuda.synchronize()
-    for _ in range(3):
-        F.fp8_gemm_bias(x8, F.E4M3, six, w8, F.E4M3, siw, None, y)
-        torch.cuda.synchronize()
-    for _ in range(3):
-        torch._scaled_mm(a8, b8.t(), scale_a=six[0], scale_b=siw[0], out_dtype=torch.bfloat16)
-        torch.cuda.synchronize()
-    print(json.dumps({"mfma_probe": "done", "gemm": [M, N, K]}))
 
 
 def traffic_probe():
@@ -147,9 +121,6 @@ def main():
     if args.traffic_probe:
         traffic_probe()
         return
-    if args.mfma_probe:
-        mfma_probe()
-        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; sharding across GPUs is described, "
                                    "not implemented (run with --gpus 1)"}))
@@ -167,6 +138,12 @@ def main():
 
     def bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.casts_only:
+        res = cast_family(F, S, torch, np, dev, bf16)
+        res["roofline_cast_transpose"] = _cast_roofline(res["cast_transpose_sweep_cold"]["8192x12288"])
+        print(json.dumps({"casts_only": res}))
+        return
 
     t0 = time.time()
     x_h = S.normal_bf16(S.seed_for(4, 0), (M, K), 1.0)
@@ -264,7 +241,7 @@ def main():
     ct_w_bytes = N * K * 4
     dct_bytes = M * N * 4 + N * 4
 
-    traffic = _traffic_record()
+    traffic = _traffic_record("gemm_fp8_qkv_counters.json", "gemm.hip")
 
     result = {
         "metric": "FP8 linear fwd+bwd TFLOP/s + cast_transpose GB/s, % of MI355X peak",
@@ -312,6 +289,7 @@ def main():
     if not args.no_extras:
         result["extras"] = extras(F, S, torch, np, dev, bf16,
                                   {"x8": x8, "w8": w8, "w8t": w8t, "dy8": dy8, "sinv": sinv})
+        result["roofline_cast_transpose"] = _cast_roofline(result["extras"]["cast_transpose_sweep_cold"]["8192x12288"])
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(x_h, w_h, b_h, dy_h)
@@ -319,19 +297,28 @@ def main():
     print(json.dumps(result))
 
 
-def _traffic_record():
-    """HBM traffic of the GEMM from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel source (its sha256 is stored with the counters); otherwise null."""
-    path = os.path.join(ROOT, "profiles", "gemm_fp8_qkv_counters.json")
-    src = os.path.join(ROOT, "fp8_delayed_scaling_amd", "csrc", "gemm.hip")
+def _traffic_record(counters, source):
+    """HBM traffic per launch from a committed rocprofv3 counter summary under profiles/, if it
+    was taken on the current kernel source (its sha256 is stored with the counters); else null."""
+    path = os.path.join(ROOT, "profiles", counters)
+    src = os.path.join(ROOT, "fp8_delayed_scaling_amd", "csrc", source)
     try:
         rec = json.load(open(path))
         h = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if rec.get("gemm_source_sha256") != h:
+        if rec.get("source_sha256", rec.get("gemm_source_sha256")) != h:
             return None
         return rec.get("traffic_bytes_per_launch")
     except (OSError, ValueError):
         return None
+
+
+def _cast_roofline(cold):
+    """Roofline entry of the cast+transpose of x [8192, 12288] (cold): 4 algorithmic bytes per
+    element (2 read, 1 + 1 written) over the kernel's average duration, against 8 TB/s."""
+    gbps = cold["GBps"]
+    return {"bound": "hbm", "kernel": "k_cast_transpose (x [8192,12288] E4M3, cold)", "achieved": gbps,
+            "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(gbps * 1e9 / HBM_PEAK, 4),
+            "traffic": _traffic_record("cast_transpose_counters.json", "cast.hip")}
 
 
 def _time_fn(torch, fn, reps=20):
@@ -342,6 +329,98 @@ def _time_fn(torch, fn, reps=20):
     e.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) / reps
+
+
+ROTATE_BYTES = 1 << 30     # traffic between two touches of one buffer set in the cold timings
+
+
+def cold_rotating(torch, calls, bytes_per_call, reps=5):
+    """Average duration (ms) of one call when its buffers are cold: `calls` are the same
+    operation on distinct buffer sets, launched round-robin back to back, so a set is touched
+    again only after the others' traffic (at least ROTATE_BYTES in total) has passed through
+    the caches.  One warm-up pass over the sets, then `reps` passes between one pair of events."""
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        for c in calls:
+            c()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / (reps * len(calls))
+
+
+def _nsets(bytes_per_call):
+    """Buffer sets for cold_rotating: the others' traffic exceeds ROTATE_BYTES, at least 3 sets."""
+    return max(3, 1 + -(-ROTATE_BYTES // bytes_per_call))
+
+
+def cast_family(F, S, torch, np, dev, bf16):
+    """Cold timings of the cast family at the sweep and backward-prep workloads: cast+transpose
+    of N(0,1) tensors with 0.1% outliers x1e3 at [1024,1024], [4096,4096], [8192,12288] (at the
+    steady-state scale 0.4); cast+amax at [8192,12288]; dbias+cast+transpose of dy [8192,4096]
+    ~N(0,0.01) (E5M2, scale 4096) and the T=3, L=1024 scale update."""
+    out = {}
+    u8 = dict(device=dev, dtype=torch.uint8)
+    f32 = dict(device=dev, dtype=torch.float32)
+    sweep = {}
+    for idx, (R, C) in enumerate([(1024, 1024), (4096, 4096), (8192, 12288)]):
+        xd = bf16(S.outlier_bf16(S.seed_for(1, idx), (R, C), 1.0))
+        nbytes = R * C * 4
+        ns = _nsets(nbytes)
+        # distinct inputs per set: copies of the one seeded tensor (same bytes, other addresses)
+        xs = [xd] + [xd.clone() for _ in range(ns - 1)]
+        sets = [(x_, torch.empty((R, C), **u8), torch.empty((C, R), **u8)) for x_ in xs]
+        sc, si, am = torch.tensor([0.4], **f32), torch.zeros(1, **f32), torch.zeros(1, **f32)
+        calls = [lambda x_=x_, o=o, ot=ot: F.fp8_cast_transpose(x_, sc, F.E4M3, o, ot, si, am) for x_, o, ot in sets]
+        ms = cold_rotating(torch, calls, nbytes)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        sweep[f"{R}x{C}"] = {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
+                             "frac_hbm": round(gbps * 1e9 / HBM_PEAK, 3), "buffer_sets": ns}
+        if R * C >= 4096 * 4096:
+            # warm, for reference: back-to-back calls on one set, the input partly cache-resident
+            msw = _time_fn(torch, calls[0], 20)
+            sweep[f"{R}x{C}"].update({"warm_us": round(msw * 1e3, 2), "warm_GBps": round(nbytes / (msw * 1e-3) / 1e9, 1)})
+        del xs, sets, calls, xd
+    out["cast_transpose_sweep_cold"] = sweep
+
+    # cast+amax (row-major only) at the large shape, cold
+    R, C = 8192, 12288
+    xd = bf16(S.outlier_bf16(S.seed_for(1, 2), (R, C), 1.0))
+    nbytes = R * C * 3
+    xs = [xd] + [xd.clone() for _ in range(_nsets(nbytes) - 1)]
+    sets = [(x_, torch.empty((R * C,), **u8)) for x_ in xs]
+    sc, si, am = torch.tensor([0.4], **f32), torch.zeros(1, **f32), torch.zeros(1, **f32)
+    ms = cold_rotating(torch, [lambda x_=x_, o=o: F.fp8_cast_amax(x_, sc, F.E4M3, o, si, am) for x_, o in sets], nbytes)
+    out["cast_amax_8192x12288_cold"] = {"us": round(ms * 1e3, 2), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                        "frac_hbm": round(nbytes / (ms * 1e-3) / HBM_PEAK, 3)}
+    del xs, sets, xd
+
+    # backward prep: dbias + cast+transpose dy [8192, 4096] E5M2, cold; scale update L=1024, T=3
+    R, C = 8192, 4096
+    dyd = bf16(S.normal_bf16(S.seed_for(3, 0), (R, C), 0.01))
+    nbytes = R * C * 4 + C * 4
+    xs = [dyd] + [dyd.clone() for _ in range(_nsets(nbytes) - 1)]
+    sets = [(x_, torch.empty((R, C), **u8), torch.empty((C, R), **u8), torch.empty(C, **f32),
+             torch.empty(F.fp8_dbias_workspace_bytes(R, C), **u8)) for x_ in xs]
+    sc, si, am = torch.tensor([4096.0], **f32), torch.zeros(1, **f32), torch.zeros(1, **f32)
+    ms = cold_rotating(torch, [lambda x_=x_, o=o, ot=ot, d=d, w=w: F.fp8_dbias_cast_transpose(x_, sc, F.E5M2, o, ot, d,
+                                                                                            w, si, am)
+                               for x_, o, ot, d, w in sets], nbytes)
+    h = torch.from_numpy(S.log_uniform_f32(S.seed_for(3, 1), 1024 * 3, 1e-3, 1e3).reshape(1024, 3)).to(dev)
+    s3, si3 = torch.ones(3, **f32), torch.ones(3, **f32)
+    F.fp8_scale_update(h, s3, si3, [0, 0, 1], 0)
+    torch.cuda.synchronize()
+    us_upd = _time_fn(torch, lambda: F.fp8_scale_update(h, s3, si3, [0, 0, 1], 0), 50) * 1e3
+    out["backward_prep"] = {"dbias_cast_transpose_8192x4096_us": round(ms * 1e3, 2),
+                            "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                            "frac_hbm": round(nbytes / (ms * 1e-3) / HBM_PEAK, 3),
+                            "scale_update_L1024_T3_us": round(us_upd, 2)}
+    del xs, sets, dyd
+    torch.cuda.empty_cache()
+    return out
 
 
 def extras(F, S, torch, np, dev, bf16, step):
@@ -365,52 +444,7 @@ def extras(F, S, torch, np, dev, bf16, step):
             ts.append(s.elapsed_time(e))
         return float(np.median(ts))
 
-    # cast+transpose sweep (steady-state scale of its outlier tensors), cold caches
-    sweep = {}
-    for idx, (R, C) in enumerate([(1024, 1024), (4096, 4096), (8192, 12288)]):
-        xh = S.outlier_bf16(S.seed_for(1, idx), (R, C), 1.0)
-        xd = bf16(xh)
-        o, ot = torch.empty((R, C), **u8), torch.empty((C, R), **u8)
-        sc, si, am = torch.tensor([0.4], **f32), torch.zeros(1, **f32), torch.zeros(1, **f32)
-        F.fp8_cast_transpose(xd, sc, F.E4M3, o, ot, si, am)
-        ms = cold_time(lambda: F.fp8_cast_transpose(xd, sc, F.E4M3, o, ot, si, am))
-        gbps = R * C * 4 / (ms * 1e-3) / 1e9
-        sweep[f"{R}x{C}"] = {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1), "frac_hbm": round(gbps * 1e9 / HBM_PEAK, 3)}
-        if R * C >= 4096 * 4096:
-            # warm, for reference: back-to-back calls, the input partly cache-resident (not at
-            # [1024, 1024], where back-to-back calls measure the host's enqueue rate instead)
-            msw = _time_fn(torch, lambda: F.fp8_cast_transpose(xd, sc, F.E4M3, o, ot, si, am), 20)
-            sweep[f"{R}x{C}"].update({"warm_us": round(msw * 1e3, 2),
-                                      "warm_GBps": round(R * C * 4 / (msw * 1e-3) / 1e9, 1)})
-        del xd, o, ot
-    out["cast_transpose_sweep_cold"] = sweep
-
-    # cast+amax (row-major only) at the same large shape, cold
-    xh = S.outlier_bf16(S.seed_for(1, 2), (8192, 12288), 1.0)
-    xd = bf16(xh)
-    o = torch.empty((8192 * 12288,), **u8)
-    sc, si, am = torch.tensor([0.4], **f32), torch.zeros(1, **f32), torch.zeros(1, **f32)
-    ms = cold_time(lambda: F.fp8_cast_amax(xd, sc, F.E4M3, o, si, am))
-    out["cast_amax_8192x12288_cold"] = {"us": round(ms * 1e3, 2), "GBps": round(8192 * 12288 * 3 / (ms * 1e-3) / 1e9, 1)}
-    del xd, o
-
-    # backward prep: dbias + cast+transpose dy [8192, 4096] E5M2; scale update L=1024, T=3
-    R, C = 8192, 4096
-    dyd = bf16(S.normal_bf16(S.seed_for(3, 0), (R, C), 0.01))
-    o, ot = torch.empty((R, C), **u8), torch.empty((C, R), **u8)
-    dbb = torch.empty(C, **f32)
-    wsb = torch.empty(F.fp8_dbias_workspace_bytes(R, C), **u8)
-    sc, si, am = torch.tensor([4096.0], **f32), torch.zeros(1, **f32), torch.zeros(1, **f32)
-    ms = cold_time(lambda: F.fp8_dbias_cast_transpose(dyd, sc, F.E5M2, o, ot, dbb, wsb, si, am))
-    h = torch.from_numpy(S.log_uniform_f32(S.seed_for(3, 1), 1024 * 3, 1e-3, 1e3).reshape(1024, 3)).to(dev)
-    s3, si3 = torch.ones(3, **f32), torch.ones(3, **f32)
-    F.fp8_scale_update(h, s3, si3, [0, 0, 1], 0)
-    torch.cuda.synchronize()
-    us_upd = _time_fn(torch, lambda: F.fp8_scale_update(h, s3, si3, [0, 0, 1], 0), 50) * 1e3
-    out["backward_prep"] = {"dbias_cast_transpose_8192x4096_us": round(ms * 1e3, 2),
-                            "GBps": round((R * C * 4 + C * 4) / (ms * 1e-3) / 1e9, 1),
-                            "scale_update_L1024_T3_us": round(us_upd, 2)}
-    del dyd, o, ot
+    out.update(cast_family(F, S, torch, np, dev, bf16))
 
     # small forward layer: eager call vs graph replay
     Ms, Ns, Ks = 128, 256, 256
@@ -505,13 +539,13 @@ def extras(F, S, torch, np, dev, bf16, step):
     # lazy transpose-cache fill of the FP8 weight [18432, 12288], cold (1 B read + 1 B written)
     Rw, Cw = 18432, 12288
     W8 = torch.randint(0, 256, (Rw, Cw), generator=torch.Generator().manual_seed(9), dtype=torch.uint8).to(dev)
-    W8t = torch.empty((Cw, Rw), **u8)
-    F.fp8_transpose(W8, W8t)
-    ms = cold_time(lambda: F.fp8_transpose(W8, W8t))
-    gbps = Rw * Cw * 2 / (ms * 1e-3) / 1e9
+    nbytes = Rw * Cw * 2
+    sets = [(W8 if k == 0 else W8.clone(), torch.empty((Cw, Rw), **u8)) for k in range(_nsets(nbytes))]
+    ms = cold_rotating(torch, [lambda a=a, b=b: F.fp8_transpose(a, b) for a, b in sets], nbytes)
+    gbps = nbytes / (ms * 1e-3) / 1e9
     out["fp8_transpose_18432x12288_cold"] = {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
                                               "frac_hbm": round(gbps * 1e9 / HBM_PEAK, 3)}
-    del W8, W8t
+    del W8, sets
 
     # GEMM writing an FP8 output with its own scale and amax capture, dgrad shape of the step
     # (M=8192, N=12288, K=18432), against the bfloat16-output GEMM on the same operands
@@ -537,75 +571,153 @@ def extras(F, S, torch, np, dev, bf16, step):
                                              "bf16_out_tflops": round(flop / (tb * 1e-3) / 1e12, 1)}
     del D8, Db
 
-    # context, not a target: the vendor library's FP8 GEMM (hipBLASLt through torch._scaled_mm)
-    # and this library's GEMM on the same forward-shape operands, timed alternately
-    A8, B8 = step["x8"], step["w8"]        # the forward operands
-    sa, sb = step["sinv"][0:1], step["sinv"][1:2]
-    Yb = torch.empty((M, N), device=dev, dtype=torch.bfloat16)
-    flop = 2.0 * M * N * K
-    try:
-        a8, b8 = A8.view(torch.float8_e4m3fn), B8.view(torch.float8_e4m3fn)
-        lib_call = lambda: torch._scaled_mm(a8, b8.t(), scale_a=step["sinv"][0], scale_b=step["sinv"][1],
-                                            out_dtype=torch.bfloat16)
-        lib_call()
-        F.fp8_gemm_bias(A8, 0, sa, B8, 0, sb, None, Yb)
-        torch.cuda.synchronize()
-        tl = to = float("inf")
-        for _ in range(3):
-            tl = min(tl, _time_fn(torch, lib_call, 5))
-            to = min(to, _time_fn(torch, lambda: F.fp8_gemm_bias(A8, 0, sa, B8, 0, sb, None, Yb), 5))
-        out["vendor_gemm_context_8192x18432x12288"] = {
-            "hipblaslt_scaled_mm_tflops": round(flop / (tl * 1e-3) / 1e12, 1),
-            "fp8ds_gemm_tflops": round(flop / (to * 1e-3) / 1e12, 1)}
-    except Exception as ex:   # the vendor path is context only
-        out["vendor_gemm_context_8192x18432x12288"] = {"error": repr(ex)[:200]}
-    del Yb, flush
+    del flush
     torch.cuda.empty_cache()
     return out
 
 
+def _host_cores():
+    return len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+
+
+def _row_blocks(R, n):
+    edges = [R * k // n for k in range(n + 1)]
+    return [(a, b) for a, b in zip(edges[:-1], edges[1:]) if b > a]
+
+
+def _oracle_ct(oracle, x, scale, fmt, nthreads, with_dbias=False):
+    """The oracle's cast+transpose (and dbias) of x, one row block per host thread (the ctypes
+    calls release the GIL): the blocks' row-major codes stacked, their transposed codes side by
+    side, the amax the largest block amax, dbias the sum of the blocks' column sums.  The
+    oracle's arithmetic per element is unchanged; only the driver splits the rows."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(ab):
+        xb = x[ab[0]:ab[1]]
+        q, qt, a, si = oracle.cast_transpose(xb, scale, fmt)
+        return q, qt, a, (oracle.dbias(xb) if with_dbias else None)
+
+    blocks = _row_blocks(x.shape[0], nthreads)
+    if len(blocks) == 1:
+        parts = [one(blocks[0])]
+    else:
+        with ThreadPoolExecutor(len(blocks)) as ex:
+            parts = list(ex.map(one, blocks))
+    q = np.concatenate([p[0] for p in parts], 0)
+    qt = np.concatenate([p[1] for p in parts], 1)
+    amax = max(float(p[2]) for p in parts)
+    db = sum(p[3] for p in parts) if with_dbias else None
+    return q, qt, amax, db
+
+
+def _oracle_gemm(oracle, A, fa, sa, B, fb, sb, bias, nthreads):
+    """The oracle's float64 GEMM with B split into row blocks (output column blocks), one per
+    host thread, each block's product on one BLAS thread; the blocks' outputs side by side."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    blocks = _row_blocks(B.shape[0], nthreads)
+
+    def one(ab):
+        return oracle.gemm_bias(A, fa, sa, B[ab[0]:ab[1]], fb, sb, None if bias is None else bias[ab[0]:ab[1]])
+
+    with ThreadPoolExecutor(len(blocks)) as ex:
+        return np.concatenate(list(ex.map(one, blocks)), 1)
+
+
 def cpu_baseline(x_h, w_h, b_h, dy_h):
-    """The oracle (as it stands) on a bounded sample of the step: 16 of the 8192 token rows of
-    x and dy with the full weight.  Single thread (the C oracle is scalar; BLAS limited to 1)."""
+    """The oracle (as it stands) on the host cores, one thread and threaded over row blocks:
+      * the cast family at full size: the small forward layer [128,256] x [256,256] with its
+        scale update (all steps), cast+transpose at [1024,1024], [4096,4096], [8192,12288], and
+        the backward prep (dbias+cast+transpose of dy [8192,4096], scale update L=1024, T=3);
+      * the training step on a bounded sample: 16 of the 8192 token rows of x and dy with the
+        full [18432,12288] weight (W cast+transpose at full size, three float64 GEMMs, dbias,
+        scale update); `value` is its GEMM FLOP rate with every host core in use.
+    A reported baseline only."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
+    import synthetic as S
 
-    rows = 16
-    xs = np.ascontiguousarray(x_h[:rows])
-    dys = np.ascontiguousarray(dy_h[:rows])
+    ncores = _host_cores()
+    res = {}
 
-    def one_step():
+    def timed(fn):
         t = time.perf_counter()
-        f = oracle.linear_fwd(xs, w_h, b_h, 1.0, 1.0)
-        bw = oracle.linear_bwd(dys, 1.0, f["x8t"], f["x_sinv"], f["w8t"], f["w_sinv"])
-        h = np.zeros((HIST_L, 3), np.float32)
-        h[0] = [f["x_amax"], f["w_amax"], bw["dy_amax"]]
-        oracle.scale_update(h, np.ones(3, np.float32), np.ones(3, np.float32), [0, 0, 1], 0)
+        fn()
         return time.perf_counter() - t
 
+    # small forward layer (all steps) + its scale update
+    xs, ws_, bs = (S.normal_bf16(S.seed_for(0, 0), (128, 256), 1.0), S.normal_bf16(S.seed_for(0, 1), (256, 256), 1.0),
+                   S.normal_bf16(S.seed_for(0, 2), (256,), 0.1))
+
+    def small():
+        f = oracle.linear_fwd(xs, ws_, bs, 1.0, 1.0, want_x_t=False)
+        h = np.zeros((16, 3), np.float32)
+        h[0] = [f["x_amax"], f["w_amax"], 0.0]
+        oracle.scale_update(h, np.ones(3, np.float32), np.ones(3, np.float32), [0, 0, 1], 0)
+
     with threadpool_limits(limits=1):
-        sec = one_step()
-    # the same sample with the float64 products on every host core the process may use (the
-    # scalar C parts of the oracle stay single-threaded)
-    ncores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
-    with threadpool_limits(limits=ncores):
-        sec_all = one_step()
+        us_small = min(timed(small) for _ in range(5)) * 1e6
+    res["small_forward_128x256x256_us"] = round(us_small, 1)
+
+    # cast+transpose sweep and backward prep at full size, 1 thread and all cores
+    sweep = {}
+    for idx, (R, C) in enumerate(CT_SHAPES):
+        xh = S.outlier_bf16(S.seed_for(1, idx), (R, C), 1.0)
+        t1 = timed(lambda: _oracle_ct(oracle, xh, 0.4, 0, 1))
+        tn = timed(lambda: _oracle_ct(oracle, xh, 0.4, 0, ncores))
+        sweep[f"{R}x{C}"] = {"GBps_1": round(R * C * 4 / t1 / 1e9, 3), "GBps_all": round(R * C * 4 / tn / 1e9, 3)}
+    res["cast_transpose_GBps"] = sweep
+    R, C = PREP_SHAPE
+    dyh = S.normal_bf16(S.seed_for(3, 0), (R, C), 0.01)
+    hh = S.log_uniform_f32(S.seed_for(3, 1), 1024 * 3, 1e-3, 1e3).reshape(1024, 3)
+
+    def prep(n):
+        _oracle_ct(oracle, dyh, 4096.0, 1, n, with_dbias=True)
+        oracle.scale_update(hh, np.ones(3, np.float32), np.ones(3, np.float32), [0, 0, 1], 0)
+
+    t1, tn = timed(lambda: prep(1)), timed(lambda: prep(ncores))
+    nb = R * C * 4 + C * 4
+    res[f"backward_prep_{R}x{C}_GBps"] = {"GBps_1": round(nb / t1 / 1e9, 3), "GBps_all": round(nb / tn / 1e9, 3)}
+
+    # the training step on 16 token rows with the full weight
+    rows = 16
+    xs16 = np.ascontiguousarray(x_h[:rows])
+    dys16 = np.ascontiguousarray(dy_h[:rows])
+
+    def step_sample(n):
+        w8, w8t, w_amax, _ = _oracle_ct(oracle, w_h, 1.0, 0, n)
+        w_sinv = oracle.scale_inv(1.0)
+        x8, x8t, x_amax, x_sinv = oracle.cast_transpose(xs16, 1.0, 0)
+        _oracle_gemm(oracle, x8, 0, x_sinv, w8, 0, w_sinv, b_h, n)                      # forward
+        dy8, dy8t, dy_amax, dy_sinv, _ = oracle.dbias_cast_transpose(dys16, 1.0, 1)
+        _oracle_gemm(oracle, dy8, 1, dy_sinv, w8t, 0, w_sinv, None, n)                   # dgrad
+        _oracle_gemm(oracle, dy8t, 1, dy_sinv, x8t, 0, x_sinv, None, n)                  # wgrad
+        h = np.zeros((HIST_L, 3), np.float32)
+        h[0] = [x_amax, w_amax, dy_amax]
+        oracle.scale_update(h, np.ones(3, np.float32), np.ones(3, np.float32), [0, 0, 1], 0)
+
+    with threadpool_limits(limits=1):
+        secn = timed(lambda: step_sample(ncores))
+    flop = 3 * 2.0 * rows * N * K
     model = ""
     try:
         with open("/proc/cpuinfo") as fh:
             model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
     except OSError:
         pass
-    flop = 3 * 2.0 * rows * N * K
-    return {"value": round(flop / sec / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "seconds": round(sec, 2),
-            "all_cores": {"value": round(flop / sec_all / 1e12, 6), "cores": ncores, "seconds": round(sec_all, 2)},
+    return {"value": round(flop / secn / 1e12, 6), "unit": "TFLOP/s", "cores": ncores, "kind": "oracle",
+            "seconds": round(secn, 2),
+            "cast_family": res,
             "cpu_model": model,
             "sample": f"one training step on {rows} of the {M} token rows of x and dy with the full "
-                      f"[{N},{K}] weight (W cast+transpose, three float64 GEMMs, dbias, scale update); "
-                      f"FLOPs counted as 3 x 2 x {rows} x {N} x {K}"}
+                      f"[{N},{K}] weight (W cast+transpose and the three float64 GEMMs split "
+                      f"into row blocks, one per host thread; dbias; scale update); FLOPs counted as 3 x 2 x {rows} x {N} x "
+                      f"{K}. cast_family: the oracle at full size (GB/s = 4 algorithmic bytes per element / s; "
+                      f"_1 one thread, _all one row block per host thread)"}
 
 
 if __name__ == "__main__":
