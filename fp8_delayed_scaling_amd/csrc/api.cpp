@@ -32,6 +32,12 @@ inline bool size_ok(int64_t rows, int64_t cols) {
     return rows <= (INT64_C(1) << 40) / cols;
 }
 
+// The cast kernels take one 256 x 256 tile per workgroup, numbered in 32 bits; a launch holds at
+// most two tensors.
+inline bool ct_tiles_ok(int64_t rows, int64_t cols) {
+    return ((rows + 255) / 256) * ((cols + 255) / 256) <= INT_MAX / 2;
+}
+
 int check_cast_common(const uint16_t *x, const float *scale, int fmt, const uint8_t *out, const float *sinv,
                       const float *amax, const float *noop) {
     if (!valid_fmt(fmt)) return FP8DS_ERR_FORMAT;
@@ -127,7 +133,7 @@ int fp8_cast_amax(const uint16_t *x, int64_t numel, const float *scale, int fmt,
 int fp8_cast_transpose(const uint16_t *x, int64_t rows, int64_t cols, const float *scale, int fmt, uint8_t *out,
                        uint8_t *out_t, float *scale_inv_out, float *amax_slot, const float *noop,
                        hipStream_t stream) {
-    if (!size_ok(rows, cols)) return FP8DS_ERR_SHAPE;
+    if (!size_ok(rows, cols) || !ct_tiles_ok(rows, cols)) return FP8DS_ERR_SHAPE;
     if (!valid_fmt(fmt)) return FP8DS_ERR_FORMAT;
     if (rows == 0 || cols == 0) return FP8DS_OK;
     int st = check_cast_common(x, scale, fmt, out, scale_inv_out, amax_slot, noop);
@@ -146,7 +152,7 @@ size_t fp8_dbias_workspace_bytes(int64_t rows, int64_t cols) {
 int fp8_dbias_cast_transpose(const uint16_t *dy, int64_t rows, int64_t cols, const float *scale, int fmt,
                              uint8_t *out, uint8_t *out_t, float *scale_inv_out, float *amax_slot, float *dbias,
                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    if (!size_ok(rows, cols)) return FP8DS_ERR_SHAPE;
+    if (!size_ok(rows, cols) || !ct_tiles_ok(rows, cols)) return FP8DS_ERR_SHAPE;
     if (!valid_fmt(fmt)) return FP8DS_ERR_FORMAT;
     if (cols == 0) return FP8DS_OK;
     if (dbias == nullptr) return FP8DS_ERR_NULL;
@@ -255,6 +261,7 @@ int fp8_linear_fwd(const uint16_t *x, const uint16_t *w, const uint16_t *bias, i
                    const float *w_scale, float *w_amax, uint8_t *w8, uint8_t *w8_t, float *w_scale_inv,
                    const float *w_noop, uint16_t *y, hipStream_t stream) {
     if (M < 0 || N < 0 || K < 0 || !size_ok(M, K) || !size_ok(N, K) || !size_ok(M, N)) return FP8DS_ERR_SHAPE;
+    if (!ct_tiles_ok(M, K) || !ct_tiles_ok(N, K)) return FP8DS_ERR_SHAPE;
     if (K % 16 != 0) return FP8DS_ERR_SHAPE;
     if (M == 0 || N == 0) return FP8DS_OK;
     if (y == nullptr || x_scale_inv == nullptr || w_scale_inv == nullptr) return FP8DS_ERR_NULL;
@@ -286,6 +293,7 @@ int fp8_linear_bwd(const uint16_t *dy, int64_t M, int64_t N, int64_t K, const fl
                    size_t workspace_bytes, const uint8_t *x8_t, const float *x_scale_inv, const uint8_t *w8_t,
                    const float *w_scale_inv, uint16_t *dx, void *dw, int dw_dtype, hipStream_t stream) {
     if (M < 0 || N < 0 || K < 0 || !size_ok(M, N) || !size_ok(M, K) || !size_ok(N, K)) return FP8DS_ERR_SHAPE;
+    if (!ct_tiles_ok(M, N)) return FP8DS_ERR_SHAPE;
     if (M % 16 != 0 || N % 16 != 0) return FP8DS_ERR_SHAPE;
     if (!valid_out(dw_dtype)) return FP8DS_ERR_FORMAT;
     if (M == 0 || N == 0 || K == 0) return FP8DS_ERR_SHAPE;

@@ -93,30 +93,51 @@ __global__ __launch_bounds__(256) void k_cast_amax(const uint16_t *__restrict__ 
 }
 
 // ------------------------------------------------------------------------------------------
-// 2-D cast + transpose (+ dbias partials).  A 512-thread block owns a 128-row x 256-column tile;
-// thread (rb = t / 32, cb = t % 32) owns the 8 x 8 micro-tile at rows 8rb.., columns 8cb...
-// (the wide tile keeps each DRAM access at 256-512 contiguous bytes; it measured ~10% faster
-// than 128 x 128).
-//   loads   : eight 16-byte row segments (one per micro-tile row; 32 lanes = 512 B per row);
-//   out     : per row, four codes from column pairs -> 8-byte store (32 lanes = 256 B per row);
-//   out_t   : per column, row pairs converted straight into dwords -> 8-byte fragment into
-//             LDS tile T[col][row] -> after a barrier each thread stores 16-byte row chunks
-//             of the transposed tile (8 lanes = 128 B per transposed row);
-//   dbias   : per-column sums of the micro-tile, reduced over the 16 row blocks through LDS in
-//             a fixed order, one partial per (row tile, column) into the workspace.
+// 2-D cast + transpose (+ dbias partials).  A 1024-thread block owns a 256 x 256 tile; thread
+// (rb = t / 32, cb = t % 32) owns the 8 x 8 micro-tile at rows 8rb.., columns 8cb...
+//   loads   : eight 16-byte row segments (32 lanes = 512 B of one row; a wave reads 2 rows);
+//   out     : each row's eight codes converted once (clamp + hardware conversion, four values
+//             per dword) -> one 8-byte store per row (32 lanes = 256 B per row);
+//   out_t   : the 8 x 8 byte block of codes transposed in registers (4 x 4 byte transposes,
+//             v_perm_b32) -> one 8-byte fragment per column into the LDS tile T[col][row] ->
+//             after a barrier 16-byte row chunks of the transposed tile (16 lanes = 256 B per
+//             transposed row);
+//   dbias   : per-column sums of the micro-tile, reduced over the 32 row blocks through LDS in
+//             a fixed order, one partial per (256-row tile, column) into the workspace.
+// With 256 rows per tile every transposed row segment is 256 contiguous bytes.  Measured on the
+// same buffers against 128-row x 256-column tiles of 512 threads: +5.3% at [8192, 12288],
+// +1.3% for the [8192, 18432] gradient, +10% at [8192, 4096], +18% at [4096, 4096] (one block
+// wave instead of two), -0.6% for the [18432, 12288] weight; 256-row tiles of 512 threads, or
+// 1024-thread blocks held to 64 registers (two blocks per CU, with spills), were slower, and
+// 512-byte transposed segments (two stacked tiles per block) gained nothing.
 // VEC: cols % 8 == 0 and rows % 16 == 0, so every 16-byte load, 8-byte store and 16-byte
 // transposed store is either wholly inside the tensor or wholly outside.  Otherwise each element
 // is loaded and stored on its own with bounds checks (same tile structure).
 // ------------------------------------------------------------------------------------------
-constexpr int kTile = 128;                // tile rows (also the dbias partial granularity)
+constexpr int kTile = 256;                // tile rows (also the dbias partial granularity)
 constexpr int kTileC = 256;               // tile columns
-constexpr int kCtThreads = (kTile / 8) * (kTileC / 8);   // 512
-// The transposed tile lives in LDS as T[col][row] (256 x 128 bytes, no padding).  The 8-byte
-// fragment of row block rb in transposed row `col` sits at slot rb ^ ((col >> 3) & 15): the
+constexpr int kCtThreads = (kTile / 8) * (kTileC / 8);   // 1024
+constexpr int kRowBlocks = kTile / 8;                    // 32
+// The transposed tile lives in LDS as T[col][row] (256 x 256 bytes, no padding).  The 8-byte
+// fragment of row block rb in transposed row `col` sits at slot rb ^ ((col >> 3) & 31): the
 // lanes that write one row block all hit different 8-byte slots, and a 16-byte read of chunk p
 // finds its two halves at slots 2p ^ g and (2p + 1) ^ g, i.e. in 16-byte chunk p ^ (g >> 1),
 // swapped when g is odd.
-__device__ __forceinline__ int t_swz(int col) { return (col >> 3) & 15; }
+__device__ __forceinline__ int t_swz(int col) { return (col >> 3) & (kRowBlocks - 1); }
+
+// 4 x 4 byte transpose: byte k of a, b, c, d is element (row 0..3, column k); o_k receives
+// column k in row order (byte 0 from a).  Two rounds of two-source byte selects.
+__device__ __forceinline__ void tr4(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t &o0, uint32_t &o1,
+                                    uint32_t &o2, uint32_t &o3) {
+    const uint32_t ab_lo = __builtin_amdgcn_perm(b, a, 0x05010400u);   // a0 b0 a1 b1
+    const uint32_t ab_hi = __builtin_amdgcn_perm(b, a, 0x07030602u);   // a2 b2 a3 b3
+    const uint32_t cd_lo = __builtin_amdgcn_perm(d, c, 0x05010400u);
+    const uint32_t cd_hi = __builtin_amdgcn_perm(d, c, 0x07030602u);
+    o0 = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u);             // a0 b0 c0 d0
+    o1 = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u);             // a1 b1 c1 d1
+    o2 = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u);
+    o3 = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);
+}
 
 // One tensor of a cast launch.  out_t == nullptr: row-major codes only (no transpose cache).
 struct CtTensor {
@@ -134,24 +155,26 @@ struct CtBatch {
     int64_t first1;
 };
 
-// Tile order.  With column tiles fastest, the ~512 blocks resident at once cover only about
-// 512 / tiles_c row tiles, so their transposed stores all fall in the same few 128-byte column
+// Tile order.  With column tiles fastest, the ~256 blocks resident at once cover only about
+// 256 / tiles_c row tiles, so their transposed stores all fall in the same few 256-byte column
 // ranges of out_t, rows of out_t being `rows` bytes apart.  When that stride is a multiple of
 // 4 KB the stores crowd onto few HBM channels.  Such tensors (rows % 4096 == 0, at least two
-// groups of 32 row tiles, and at least 32 column tiles, i.e. fewer than 16 row tiles in flight
-// in the default order) take their tiles in groups of 32 row tiles, row tiles fastest inside a
-// group.  Measured against the default order on the same buffers: +1.5-3.4% at [8192, 12288]
-// and [12288, 12288], +6.8% at [16384, 12288], +9-11% for the [8192, 18432] E5M2 gradient;
-// grouping [18432, 12288] (stride not a multiple of 4 KB) was 3-9% slower, [4096, 12288] (one
-// group) 2.8% slower and [8192, 4096] (16 column tiles) 5% slower, so those keep the default.
-constexpr int kRowGroup = 32;
-__device__ __forceinline__ void ct_tile_of(int64_t block, int64_t rows, int64_t tiles_c, int64_t &tile_r,
-                                           int64_t &tile_c) {
-    if (rows % 4096 == 0 && rows >= 2 * kRowGroup * kTile && tiles_c >= 32) {
-        // rows is a multiple of 32 tiles, so every group is full
-        const int64_t per = kRowGroup * tiles_c, g = block / per, local = block - g * per;
-        tile_r = g * kRowGroup + local % kRowGroup;
-        tile_c = local / kRowGroup;
+// bands of 16 row tiles, and at least 32 column tiles) take their tiles in bands of 16 row
+// tiles (4096 rows), row tiles fastest inside a band.  Measured on the same buffers against
+// column tiles fastest: +2% at [8192, 12288], +11% for the [8192, 18432] gradient, +5% at
+// [12288, 12288], +9% at [16384, 12288]; against bands of 8 or 32 row tiles: 3-13% and 6-12%
+// faster at those shapes; against a band order that alternates blocks between two bands, or a
+// pseudo-random order, 4-10% faster.  The [18432, 12288] weight (stride not a multiple of 4 KB)
+// and the 16-column-tile [8192, 4096] gradient are faster in the default order.
+constexpr int kRowBand = 16;
+// (32-bit arithmetic: the host rejects tensors of 2^31 tiles or more.)
+__device__ __forceinline__ void ct_tile_of(uint32_t block, int64_t rows, uint32_t tiles_c, uint32_t &tile_r,
+                                           uint32_t &tile_c) {
+    if (rows % 4096 == 0 && rows >= 2 * kRowBand * kTile && tiles_c >= 32) {
+        // rows is a multiple of 16 tiles, so every band is full
+        const uint32_t per = kRowBand * tiles_c, g = block / per, local = block - g * per;
+        tile_r = g * kRowBand + local % kRowBand;
+        tile_c = local / kRowBand;
     } else {
         tile_r = block / tiles_c;
         tile_c = block - tile_r * tiles_c;
@@ -161,31 +184,46 @@ __device__ __forceinline__ void ct_tile_of(int64_t block, int64_t rows, int64_t 
 template <int FMT, bool VEC, bool DBIAS>
 __global__ __launch_bounds__(kCtThreads) void k_cast_transpose(const CtBatch batch, float *__restrict__ partial) {
     __shared__ __align__(16) uint8_t tT[kTileC * kTile];
-    __shared__ float csum[DBIAS ? 16 * kTileC : 1];
+    __shared__ float csum[DBIAS ? kRowBlocks * kTileC : 1];
     __shared__ uint32_t red[kCtThreads / 64];
+    // Both tensors' fields are kernel arguments: selecting values (not a pointer to one tensor)
+    // lets every argument load go out in one round, and the first input loads follow it.
     const bool second = (int64_t)blockIdx.x >= batch.first1;
-    const CtTensor &T = second ? batch.t[1] : batch.t[0];
-    const uint16_t *__restrict__ x = T.x;
-    const int64_t rows = T.rows, cols = T.cols;
-    uint8_t *__restrict__ out = T.out;
-    uint8_t *__restrict__ out_t = T.out_t;
-    if (T.noop != nullptr && *T.noop == 1.0f) return;
+    const uint16_t *__restrict__ x = second ? batch.t[1].x : batch.t[0].x;
+    const int64_t rows = second ? batch.t[1].rows : batch.t[0].rows;
+    const int64_t cols = second ? batch.t[1].cols : batch.t[0].cols;
+    uint8_t *__restrict__ out = second ? batch.t[1].out : batch.t[0].out;
+    uint8_t *__restrict__ out_t = second ? batch.t[1].out_t : batch.t[0].out_t;
+    const float *noop = second ? batch.t[1].noop : batch.t[0].noop;
+    const float *scale_p = second ? batch.t[1].scale : batch.t[0].scale;
+    float *amax_slot = second ? batch.t[1].amax_slot : batch.t[0].amax_slot;
+    float *sinv_out = second ? batch.t[1].sinv_out : batch.t[0].sinv_out;
+    const float s = *scale_p;
+    const float skip_flag = noop != nullptr ? *noop : 0.0f;
 
-    const float s = *T.scale;
     const int t = threadIdx.x;
     const int rb = t >> 5, cb = t & 31;
-    const int64_t block = (int64_t)blockIdx.x - (second ? batch.first1 : 0);
-    const int64_t tiles_c = (cols + kTileC - 1) / kTileC;
-    int64_t tile_r, tile_c;
+    const uint32_t block = blockIdx.x - (second ? (uint32_t)batch.first1 : 0u);
+    const uint32_t tiles_c = (uint32_t)((cols + kTileC - 1) / kTileC);
+    uint32_t tile_r, tile_c;
     ct_tile_of(block, rows, tiles_c, tile_r, tile_c);
-    const int64_t r0 = tile_r * kTile;
-    const int64_t c0 = tile_c * kTileC;
+    const int64_t r0 = (int64_t)tile_r * kTile;
+    const int64_t c0 = (int64_t)tile_c * kTileC;
     const int64_t row = r0 + rb * 8;   // first row of the micro-tile
     const int64_t col = c0 + cb * 8;   // first column of the micro-tile
+    // Interior tile (block-uniform): every access of the 16-byte path is in bounds, so loads and
+    // stores go out unconditionally (per-access checks put each one in a branch of its own).
+    const bool full = VEC && r0 + kTile <= rows && c0 + kTileC <= cols;
 
     // ---- load 8 rows x 8 columns (bfloat16 pairs in dwords: w[r][0..3])
     uint32_t w[8][4];
-    if constexpr (VEC) {
+    if (full) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + (row + r) * cols + col));
+            w[r][0] = v.x; w[r][1] = v.y; w[r][2] = v.z; w[r][3] = v.w;
+        }
+    } else if constexpr (VEC) {
         const bool cin = col < cols;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
@@ -211,6 +249,15 @@ __global__ __launch_bounds__(kCtThreads) void k_cast_transpose(const CtBatch bat
         }
     }
 
+    // The noop flag is tested only now, so the input loads do not wait behind its round trip
+    // (the compiler would otherwise sink them below the early exit); a skipped cast drains its
+    // loads before it ends and writes nothing.
+    __asm__ volatile("" ::: "memory");
+    if (skip_flag == 1.0f) {
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
+    }
+
     // ---- amax of the micro-tile (out-of-range elements are zero)
     uint32_t tam = 0;
 #pragma unroll
@@ -234,66 +281,39 @@ __global__ __launch_bounds__(kCtThreads) void k_cast_transpose(const CtBatch bat
         }
     }
 
-    // ---- scaled, clamped values y[r][c]
-    uint32_t orow[8][2];   // row-major codes: row r, columns 0-3 / 4-7
-    uint32_t ocol[8][2];   // transposed codes: column c, rows 0-3 / 4-7
+    // ---- row codes: orow[r][h] = the four codes of row r, columns 4h .. 4h+3
+    uint32_t orow[8][2];
     if (scale_is_plain(s) && mag < 0x7F80u) {
-        float y[8][8];
 #pragma unroll
         for (int r = 0; r < 8; ++r)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                y[r][2 * c] = clamp_fmt<FMT>(bf16_lo(w[r][c]) * s);
-                y[r][2 * c + 1] = clamp_fmt<FMT>(bf16_hi(w[r][c]) * s);
-            }
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            orow[r][0] = pack4<FMT>(y[r][0], y[r][1], y[r][2], y[r][3]);
-            orow[r][1] = pack4<FMT>(y[r][4], y[r][5], y[r][6], y[r][7]);
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            ocol[c][0] = pack4<FMT>(y[0][c], y[1][c], y[2][c], y[3][c]);
-            ocol[c][1] = pack4<FMT>(y[4][c], y[5][c], y[6][c], y[7][c]);
-        }
+            for (int h = 0; h < 2; ++h)
+                orow[r][h] = pack4<FMT>(clamp_fmt<FMT>(bf16_lo(w[r][2 * h]) * s), clamp_fmt<FMT>(bf16_hi(w[r][2 * h]) * s),
+                                        clamp_fmt<FMT>(bf16_lo(w[r][2 * h + 1]) * s),
+                                        clamp_fmt<FMT>(bf16_hi(w[r][2 * h + 1]) * s));
     } else {
-        uint32_t e[8][8];
 #pragma unroll
         for (int r = 0; r < 8; ++r)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                e[r][2 * c] = encode_exact<FMT>(bf16_lo(w[r][c]) * s);
-                e[r][2 * c + 1] = encode_exact<FMT>(bf16_hi(w[r][c]) * s);
-            }
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            orow[r][0] = e[r][0] | (e[r][1] << 8) | (e[r][2] << 16) | (e[r][3] << 24);
-            orow[r][1] = e[r][4] | (e[r][5] << 8) | (e[r][6] << 16) | (e[r][7] << 24);
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            ocol[c][0] = e[0][c] | (e[1][c] << 8) | (e[2][c] << 16) | (e[3][c] << 24);
-            ocol[c][1] = e[4][c] | (e[5][c] << 8) | (e[6][c] << 16) | (e[7][c] << 24);
-        }
-    }
-
-    const bool want_t = out_t != nullptr;   // block-uniform
-    // ---- transposed fragments into LDS: T[cb*8 + c][rb*8 .. rb*8+7]
-    if (want_t)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const int tc = cb * 8 + c;
-        u32x2 v = {ocol[c][0], ocol[c][1]};
-        *reinterpret_cast<u32x2 *>(&tT[tc * kTile + ((rb ^ t_swz(tc)) << 3)]) = v;
+            for (int h = 0; h < 2; ++h)
+                orow[r][h] = encode_exact<FMT>(bf16_lo(w[r][2 * h]) * s) |
+                             (encode_exact<FMT>(bf16_hi(w[r][2 * h]) * s) << 8) |
+                             (encode_exact<FMT>(bf16_lo(w[r][2 * h + 1]) * s) << 16) |
+                             (encode_exact<FMT>(bf16_hi(w[r][2 * h + 1]) * s) << 24);
     }
 
     // ---- row-major codes straight to global memory
-    if constexpr (VEC) {
+    if (full) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            u32x2 v = {orow[r][0], orow[r][1]};
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(out + (row + r) * cols + col));
+        }
+    } else if constexpr (VEC) {
         if (col < cols) {
 #pragma unroll
             for (int r = 0; r < 8; ++r)
-                if (row + r < rows)
-                {
+                if (row + r < rows) {
                     u32x2 v = {orow[r][0], orow[r][1]};
                     __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(out + (row + r) * cols + col));
                 }
@@ -307,20 +327,42 @@ __global__ __launch_bounds__(kCtThreads) void k_cast_transpose(const CtBatch bat
                     out[(row + r) * cols + col + c] = (uint8_t)(orow[r][c >> 2] >> (8 * (c & 3)));
     }
 
+    const bool want_t = out_t != nullptr;   // block-uniform
+    // ---- column codes by byte transposes: ocol[c][h] = rows 4h .. 4h+3 of column c; then the
+    // transposed fragments into LDS: T[cb*8 + c][rb*8 .. rb*8+7]
+    if (want_t) {
+        uint32_t ocol[8][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            tr4(orow[0][h], orow[1][h], orow[2][h], orow[3][h], ocol[4 * h][0], ocol[4 * h + 1][0], ocol[4 * h + 2][0],
+                ocol[4 * h + 3][0]);
+            tr4(orow[4][h], orow[5][h], orow[6][h], orow[7][h], ocol[4 * h][1], ocol[4 * h + 1][1], ocol[4 * h + 2][1],
+                ocol[4 * h + 3][1]);
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int tc = cb * 8 + c;
+            u32x2 v = {ocol[c][0], ocol[c][1]};
+            *reinterpret_cast<u32x2 *>(&tT[tc * kTile + ((rb ^ t_swz(tc)) << 3)]) = v;
+        }
+    }
+
     __syncthreads();
 
-    // ---- transposed tile out: 256 transposed rows x 128 bytes, 16-byte chunks
+    // ---- transposed tile out: 256 transposed rows x 256 bytes, 16-byte chunks
     if (want_t)
 #pragma unroll
     for (int i = 0; i < (kTileC * kTile / 16) / kCtThreads; ++i) {
         const int q = t + kCtThreads * i;
-        const int tr = q >> 3, part = q & 7;          // transposed row (= tile column), chunk
+        const int tr = q >> 4, part = q & 15;          // transposed row (= tile column), chunk
         const int64_t orow_g = c0 + tr;                 // row of out_t
         const int64_t ocol_g = r0 + part * 16;          // first column of out_t in this chunk
         const int g = t_swz(tr);
         u32x4 v = *reinterpret_cast<const u32x4 *>(&tT[tr * kTile + ((part ^ (g >> 1)) << 4)]);
         if (g & 1) v = v.zwxy;
-        if constexpr (VEC) {
+        if (full) {
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(out_t + orow_g * rows + ocol_g));
+        } else if constexpr (VEC) {
             if (orow_g < cols && ocol_g < rows)
                 __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(out_t + orow_g * rows + ocol_g));
         } else {
@@ -333,30 +375,30 @@ __global__ __launch_bounds__(kCtThreads) void k_cast_transpose(const CtBatch bat
         }
     }
 
-    // ---- dbias partial of this row tile: fixed-order sum over the 16 row blocks
+    // ---- dbias partial of this row tile: fixed-order sum over the 32 row blocks
     if constexpr (DBIAS) {
         if (t < kTileC) {
             float acc = 0.f;
 #pragma unroll
-            for (int b = 0; b < 16; ++b) acc += csum[b * kTileC + t];
-            if (c0 + t < cols) partial[tile_r * cols + c0 + t] = acc;
+            for (int b = 0; b < kRowBlocks; ++b) acc += csum[b * kTileC + t];
+            if (c0 + t < cols) partial[(int64_t)tile_r * cols + c0 + t] = acc;
         }
     }
 
     // ---- amax: one atomic per block; inverse scale from block (0, 0)
     uint32_t bm = block_max_u32<kCtThreads>(mag, red);
     if (t == 0) {
-        fold_amax(T.amax_slot, bm);
-        if (block == 0 && T.sinv_out != nullptr) *T.sinv_out = 1.0f / s;
+        fold_amax(amax_slot, bm);
+        if (block == 0 && sinv_out != nullptr) *sinv_out = 1.0f / s;
     }
 }
 
 // dbias[j] = sum over row tiles of partial[tile][j], in a fixed order: a 256-thread block owns
 // 64 columns; thread (g = t / 64, c = t % 64) sums tiles g, g + 4, g + 8, ... in increasing order,
 // then the four partial sums are added in the order g = 0, 1, 2, 3.  The order depends only on
-// the number of tiles, so the result is the same run to run.  Sixteen loads are issued before
-// their sums (same order), so a thread waits for one memory round trip per 16 tiles instead of
-// one per tile.
+// the number of tiles, so the result is the same run to run.  A thread's loads go out sixteen at
+// a time before their sums (same order; the last batch's missing tiles are skipped), so it waits
+// for one memory round trip per 16 tiles instead of one per tile.
 __global__ __launch_bounds__(256) void k_dbias_reduce(const float *__restrict__ partial, int64_t ntiles,
                                                       int64_t cols, float *__restrict__ dbias) {
     __shared__ float part[4][64];
@@ -365,15 +407,14 @@ __global__ __launch_bounds__(256) void k_dbias_reduce(const float *__restrict__ 
     float acc = 0.f;
     if (j < cols) {
         const float *__restrict__ p = partial + j;
-        int64_t i = g;
-        for (; i + 60 < ntiles; i += 64) {
+        for (int64_t i = g; i < ntiles; i += 64) {
             float v[16];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) v[u] = p[(i + 4 * u) * cols];
+            for (int u = 0; u < 16; ++u) v[u] = i + 4 * u < ntiles ? p[(i + 4 * u) * cols] : 0.f;
 #pragma unroll
-            for (int u = 0; u < 16; ++u) acc += v[u];
+            for (int u = 0; u < 16; ++u)
+                if (i + 4 * u < ntiles) acc += v[u];
         }
-        for (; i < ntiles; i += 4) acc += p[i * cols];
     }
     part[g][c] = acc;
     __syncthreads();

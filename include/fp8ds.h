@@ -135,7 +135,7 @@ int fp8_dbias_cast_transpose(const uint16_t *dy, int64_t rows, int64_t cols, con
  * workspace: the partial column sums go to a static device array of
  * FP8DS_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on until the process
  * ends.  Calls nothing that allocates.  Limit: fp8_dbias_workspace_bytes(rows, cols) <=
- * FP8DS_NOALLOC_SCRATCH_BYTES (8 MiB: e.g. [8192, 16384] needs 4 MiB, [8192, 32768] 8 MiB),
+ * FP8DS_NOALLOC_SCRATCH_BYTES (8 MiB: e.g. [8192, 16384] needs 2 MiB, [8192, 65536] 8 MiB),
  * else FP8DS_ERR_SCRATCH and nothing is launched.  All calls on one GPU share its array and
  * each call overwrites it, so calls that overlap in time on one GPU (on two streams, or from
  * two host threads) race: serialise them.

@@ -53,12 +53,15 @@ def test_cast_validation():
     assert L.fp8_cast_transpose(A16, 4, 4, A16, 0, A16, None, None, None, None, None) == -1   # NULL out_t
     assert L.fp8_cast_transpose(A16, 4, -4, A16, 0, A16, A16, None, None, None, None) == -2
     assert L.fp8_cast_transpose(A16, 4, 4, A16, 0, A16, A16 + 8, None, None, None, None) == -3
+    # 2^40 elements in one row: 2^32 tiles of 256 x 256, more than a launch numbers
+    assert L.fp8_cast_transpose(A16, 1, 1 << 40, A16, 0, A16, A16, None, None, None, None) == -2
+    assert L.fp8_dbias_cast_transpose(A16, 1, 1 << 40, A16, 1, A16, A16, None, None, A16, A16, 1 << 50, None) == -2
 
 
 def test_dbias_validation():
     L = F.lib()
     need = F.fp8_dbias_workspace_bytes(300, 100)
-    assert need == 3 * 100 * 4       # one float per (128-row block, column)
+    assert need == 2 * 100 * 4       # one float per (256-row block, column)
     assert F.fp8_dbias_workspace_bytes(0, 100) == 0
     assert L.fp8_dbias_cast_transpose(A16, 300, 100, A16, 1, A16, A16, None, None, A16, None, 0, None) == -5
     assert L.fp8_dbias_cast_transpose(A16, 300, 100, A16, 1, A16, A16, None, None, A16, A16, need - 4, None) == -5
@@ -71,9 +74,9 @@ def test_dbias_noalloc_rejects_sizes_beyond_its_scratch():
     f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     f.restype = ctypes.c_int
-    # 64 row blocks x 40000 columns x 4 bytes = 10.24 MB of partials > 8 MiB: rejected, nothing launched
-    assert F.fp8_dbias_workspace_bytes(8192, 40000) > 8 << 20
-    assert f(A16, 8192, 40000, A16, 1, A16, A16, None, None, A16, None) == -8
+    # 32 row blocks x 80000 columns x 4 bytes = 10.24 MB of partials > 8 MiB: rejected, nothing launched
+    assert F.fp8_dbias_workspace_bytes(8192, 80000) > 8 << 20
+    assert f(A16, 8192, 80000, A16, 1, A16, A16, None, None, A16, None) == -8
     assert f(A16, -1, 100, A16, 1, A16, A16, None, None, A16, None) == -2
 
 

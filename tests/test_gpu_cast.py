@@ -92,7 +92,7 @@ def test_cast_transpose_parity(fmt, shape):
 @pytest.mark.parametrize("fmt,shape", [(F.E4M3, (8192, 8200)), (F.E5M2, (8192, 8193)), (F.E4M3, (12288, 8448))])
 def test_cast_transpose_grouped_tile_order(fmt, shape):
     """Tensors whose rows are a multiple of 4096 (at least 8192) with at least 32 column tiles
-    take their tiles in groups of 32 row tiles: every tile is covered once, with a ragged column
+    take their tiles in bands of 16 row tiles: every tile is covered once, with a ragged column
     tail on the 16-byte path (8200 columns) and on the element-wise path (8193 columns)."""
     print(f"cast_transpose grouped order fmt={fmt} shape={shape}", flush=True)
     xh = S.outlier_bf16(S.seed_for(13, 11 + shape[1] % 5), shape, 1.0)
@@ -196,7 +196,7 @@ def test_dbias_cast_transpose_parity(shape):
 
 @pytest.mark.parametrize("R", [8192, 17297])
 def test_dbias_constant_columns_exact(R):
-    """0.5 everywhere: every partial and final sum is exact, so dbias = R / 2 exactly (136 row
+    """0.5 everywhere: every partial and final sum is exact, so dbias = R / 2 exactly (68 row
     tiles for R = 17297: whole 16-tile batches of the reduction plus single-tile remainders)."""
     C = 64
     dyh = np.full((R, C), 0x3F00, np.uint16)

@@ -430,7 +430,7 @@ def test_weight_caching_across_microbatches_in_a_graph():
 def test_linear_fwd_grouped_casts(shape, with_xt):
     """fp8_linear_fwd casts x and W in one launch when both take the same code path (rows % 16
     and cols % 8), else in two; with and without x's transpose cache.  Codes, transposes, amaxes,
-    inverse scales and y against the oracle.  At [8192, 8448] x takes its tiles in groups of 32
+    inverse scales and y against the oracle.  At [8192, 8448] x takes its tiles in bands of 16
     row tiles while W, in the same launch, keeps the default order."""
     M, N, K = shape
     print(f"linear fwd grouped casts M={M} N={N} K={K} x_t={with_xt}", flush=True)

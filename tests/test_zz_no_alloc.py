@@ -70,7 +70,7 @@ def test_noalloc_two_calls_second_smaller(shapes):
 
 
 def test_noalloc_rejects_beyond_scratch():
-    R, C = 8192, 40000          # 10.24 MB of partials > the 8 MiB scratch
+    R, C = 8192, 80000          # 10.24 MB of partials > the 8 MiB scratch
     dy = torch.zeros((R, 16), dtype=torch.bfloat16, device=DEV)   # never read: rejected first
     st = _abi()(dy.data_ptr(), R, C, dy.data_ptr(), F.E5M2, dy.data_ptr(), dy.data_ptr(), None, None,
                 dy.data_ptr(), None)
