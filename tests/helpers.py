@@ -48,3 +48,27 @@ def gemm_close(got: np.ndarray, ref: np.ndarray, bf16_out: bool, scale_ref: floa
         raise AssertionError(f"GEMM mismatch at {i}: got {got[i]} ref {ref[i]} err {err[i]} bound "
                              f"{np.broadcast_to(bound, err.shape)[i]} (max|R| {big})")
     return float(err.max() / big) if big else 0.0
+
+
+def oracle_cast_transpose_rows(oracle, x, scale, fmt, nthreads=16, with_dbias=False):
+    """The oracle's cast+transpose (and float64 dbias) of a large 2-D tensor, one row block per
+    host thread (the oracle's C calls release the GIL): the blocks' codes stacked, their
+    transposed codes side by side, the largest block amax, the sum of the blocks' column sums.
+    Every element goes through the oracle's own per-element code; only the rows are split."""
+    from concurrent.futures import ThreadPoolExecutor
+    R = x.shape[0]
+    n = max(1, min(nthreads, R // 256))
+    edges = [R * k // n for k in range(n + 1)]
+
+    def one(k):
+        xb = x[edges[k]:edges[k + 1]]
+        q, qt, a, si = oracle.cast_transpose(xb, scale, fmt)
+        return q, qt, a, si, (oracle.dbias(xb) if with_dbias else None)
+
+    with ThreadPoolExecutor(n) as ex:
+        parts = list(ex.map(one, range(n)))
+    q = np.concatenate([p[0] for p in parts], 0)
+    qt = np.concatenate([p[1] for p in parts], 1)
+    amax = max(np.float32(p[2]) for p in parts)
+    db = sum(p[4] for p in parts) if with_dbias else None
+    return q, qt, np.float32(amax), parts[0][3], db
