@@ -70,7 +70,11 @@ def parse():
 def traffic_probe():
     """One plain copy of 1 GiB (known traffic: 1 GiB read + 1 GiB written), one forward GEMM
     launch at the QKV shape, one cast+transpose of x [8192,12288] and one dbias+cast+transpose of
-    dy [8192,4096], nothing else on the GPU, so per-dispatch counters can be compared."""
+    dy [8192,4096], nothing else on the GPU, so per-dispatch counters can be compared.  Last, a
+    GEMM whose operand reads are known: A [16384, 12288] against B [256, 12288], 64 tiles of one
+    tile column, so each A byte is read by one workgroup only (201.3 MB) and B (3.1 MB) by at
+    most the 8 L2s: the GEMM's direct-to-LDS buffer loads must read between 204.5 and 226.5 MB
+    below the L2, which checks the counter scaling the copy calibrates for this access type."""
     import torch
 
     import fp8_delayed_scaling_amd as F
@@ -108,8 +112,17 @@ def traffic_probe():
     torch.cuda.synchronize()
     F.fp8_dbias_cast_transpose(dy, torch.full((1,), 4096.0, device=dev), F.E5M2, d8, d8t, db, ws, sinv, am)
     torch.cuda.synchronize()
+    del dy, d8, d8t, db, ws
+    Mc, Nc = 16384, 256
+    a8 = (torch.randint(0, 256, (Mc, K), dtype=torch.uint8, device=dev, generator=gd) & 0xF7)
+    b8 = (torch.randint(0, 256, (Nc, K), dtype=torch.uint8, device=dev, generator=gd) & 0xF7)
+    yc = torch.empty((Mc, Nc), device=dev, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    F.fp8_gemm_bias(a8, F.E4M3, one, b8, F.E4M3, one, None, yc)
+    torch.cuda.synchronize()
     print(json.dumps({"traffic_probe": "done", "copy_bytes_each_way": 1 << 30, "gemm": [M, N, K],
-                      "cast_transpose": [M, K], "dbias_cast_transpose": [R, C]}))
+                      "cast_transpose": [M, K], "dbias_cast_transpose": [R, C],
+                      "calibration_gemm": [Mc, Nc, K]}))
 
 
 def log(*a):
