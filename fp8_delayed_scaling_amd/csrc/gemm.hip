@@ -201,14 +201,52 @@ struct Quads16 {
             for (int i = 0; i < 8; ++i) {
                 if (i * 16 < RLO || i * 16 >= RHI) continue;
                 float v[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    v[u] = dequant_bias(acc[i][j][u], sa, sb,
-                                        has_bias ? __uint_as_float((uint32_t)braw[j][u >> 1][u & 1] << 16) : 0.f);
+                values(i, j, v);
                 f(i * 16 + r16, j * 4 + g, v);
             }
     }
+    // the four values of MFMA tile (i, j) this lane holds
+    __device__ __forceinline__ void values(int i, int j, float (&v)[4]) const {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            v[u] = dequant_bias(acc[i][j][u], sa, sb,
+                                has_bias ? __uint_as_float((uint32_t)braw[j][u >> 1][u & 1] << 16) : 0.f);
+    }
 };
+
+// float32 output of a wave's 128 x 128 sub-tile straight from the 16 x 16 x 128 accumulators.
+// In MFMA tiles (i, j) and (i, j + 1), row r of the pair is 128 contiguous bytes: 64 from the four
+// lanes (r, g) of tile j and 64 from the same lanes of tile j + 1.  Lanes r and r ^ 8 (the same
+// 16-lane DPP row) swap one of their two 16-byte quads (lanes r < 8 send tile j + 1, lanes r >= 8
+// send tile j), so each store instruction writes eight rows as whole 128-byte lines: the first
+// rows 0-7 of the pair (lanes r < 8 the left halves, lanes r >= 8 the right halves of rows r - 8),
+// the second rows 8-15.  Interior sub-tiles with 16-byte aligned rows only.
+__device__ __forceinline__ float dpp_swap8(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true));   // row_ror:8
+}
+__device__ __forceinline__ void store_f32_direct(const Quads16 &q, float *__restrict__ D, int64_t ldd, int row0,
+                                                 int col0) {
+    const int r16 = q.lane & 15, g = q.lane >> 4;
+    const bool hi = r16 >= 8;
+    const int rr = r16 & 7;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int jp = 0; jp < 4; ++jp) {
+            float t0[4], t1[4], x[4];
+            q.values(i, 2 * jp, t0);
+            q.values(i, 2 * jp + 1, t1);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[u] = dpp_swap8(hi ? t0[u] : t1[u]);
+            const int col = col0 + 16 * (2 * jp + (hi ? 1 : 0)) + 4 * g;
+            float *pa = D + (int64_t)(row0 + i * 16 + rr) * ldd + col;
+            float *pb = pa + 8 * ldd;
+            const f32x4 va = hi ? f32x4{x[0], x[1], x[2], x[3]} : f32x4{t0[0], t0[1], t0[2], t0[3]};
+            const f32x4 vb = hi ? f32x4{t1[0], t1[1], t1[2], t1[3]} : f32x4{x[0], x[1], x[2], x[3]};
+            __builtin_nontemporal_store(va, reinterpret_cast<f32x4 *>(pa));
+            __builtin_nontemporal_store(vb, reinterpret_cast<f32x4 *>(pb));
+        }
+}
 
 // Epilogue of the pipelined kernels.  Each wave scales, adds the bias and rounds its 128 x 128
 // sub-tile into its own 32 KB of LDS, then writes whole rows with 16-byte streaming
@@ -251,6 +289,14 @@ __device__ __forceinline__ void epilogue_staged(const Q &quads, float ds, void *
             }
         }
     } else if constexpr (OUT == 1) {
+        // interior 16 x 16 x 128 sub-tiles: straight from the accumulators (same-process A/B on
+        // the wgrad shape: +0.5% against the staged passes below, identical bits)
+        if constexpr (std::is_same_v<Q, Quads16>) {
+            if (vec_ok && row0 + 128 <= M && col0 + 128 <= N) {
+                store_f32_direct(quads, reinterpret_cast<float *>(D), ldd, row0, col0);
+                return;
+            }
+        }
         auto pass = [&](auto hc) {
             constexpr int h = decltype(hc)::value;
             quads.template visit<h * 64, h * 64 + 64>([&](int r, int sl, const float (&v)[4]) {
