@@ -108,7 +108,7 @@ def traffic_probe():
     dy = (torch.randn((R, C), device=dev, generator=gd) * 0.01).to(torch.bfloat16)
     d8, d8t = torch.empty((R, C), dtype=torch.uint8, device=dev), torch.empty((C, R), dtype=torch.uint8, device=dev)
     db = torch.empty(C, device=dev)
-    ws = torch.empty(F.fp8_dbias_workspace_bytes(R, C), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(F.fp8_dbias_workspace_bytes(R, C), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     F.fp8_dbias_cast_transpose(dy, torch.full((1,), 4096.0, device=dev), F.E5M2, d8, d8t, db, ws, sinv, am)
     torch.cuda.synchronize()
@@ -179,7 +179,7 @@ def main():
     dx = torch.empty((M, K), device=dev, dtype=torch.bfloat16)
     dw = torch.empty((N, K), **f32)
     db = torch.empty(N, **f32)
-    ws = torch.empty(F.fp8_dbias_workspace_bytes(M, N), **u8)
+    ws = torch.zeros(F.fp8_dbias_workspace_bytes(M, N), **u8)
     fmts = [F.E4M3, F.E4M3, F.E5M2]
 
     names = ["cast_transpose_x", "cast_transpose_w", "gemm_fwd", "dbias_cast_transpose_dy", "gemm_dgrad",
@@ -417,7 +417,7 @@ def cast_family(F, S, torch, np, dev, bf16):
     nbytes = R * C * 4 + C * 4
     xs = [dyd] + [dyd.clone() for _ in range(_nsets(nbytes) - 1)]
     sets = [(x_, torch.empty((R, C), **u8), torch.empty((C, R), **u8), torch.empty(C, **f32),
-             torch.empty(F.fp8_dbias_workspace_bytes(R, C), **u8)) for x_ in xs]
+             torch.zeros(F.fp8_dbias_workspace_bytes(R, C), **u8)) for x_ in xs]
     sc, si, am = torch.tensor([4096.0], **f32), torch.zeros(1, **f32), torch.zeros(1, **f32)
     ms = cold_rotating(torch, [lambda x_=x_, o=o, ot=ot, d=d, w=w: F.fp8_dbias_cast_transpose(x_, sc, F.E5M2, o, ot, d,
                                                                                             w, si, am)

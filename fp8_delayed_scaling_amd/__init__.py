@@ -181,7 +181,10 @@ def fp8_dbias_workspace_bytes(rows: int, cols: int) -> int:
 
 def fp8_dbias_cast_transpose(dy, scale, fmt, out, out_t, dbias, workspace, scale_inv_out=None, amax_slot=None,
                              stream=None):
-    """dbias = column sums of ``dy`` plus its cast+transpose (see include/fp8ds.h)."""
+    """dbias = column sums of ``dy`` plus its cast+transpose (see include/fp8ds.h).
+
+    ``workspace``: at least ``fp8_dbias_workspace_bytes(rows, cols)`` bytes, zero-filled before
+    its first use (``torch.zeros``); every call leaves its counter bytes zero again."""
     _want(dy, _BF16, "dy", required=True)
     R, C = dy.shape
     _want(dbias, _F32, "dbias", shape=(C,), required=True)

@@ -11,6 +11,9 @@
 // exchanging 8-byte fragments through LDS, so both outputs leave in coalesced stores.
 // The amax is a packed 16-bit integer max of the bfloat16 magnitudes, reduced per wave and
 // per block, with one atomic per block.
+#include <algorithm>
+
+#include "../../include/fp8ds.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -416,6 +419,226 @@ __global__ __launch_bounds__(256) void k_dbias_reduce(const float *__restrict__ 
 }
 
 // ------------------------------------------------------------------------------------------
+// dbias + cast + transpose in one launch, for tensors of whole 256 x 256 tiles that take at
+// most two tiles per CU (the bias gradient of a narrow layer, e.g. dy [8192, 4096]: 512 tiles).
+// With that few tiles the two-kernel form above pays twice for ramp-up and drain (two waves of
+// blocks, then the reduction launch); here one block per CU works through the row tiles of one
+// 256-column strip, and the column sums are finished inside the same launch:
+//   * block b owns strip b % tiles_c and the row tiles slot, slot + nslots, ... (slot = b /
+//     tiles_c); each tile's eight rows per thread are converted row by row as they are consumed
+//     (the column sums folded in), and the next tile's rows are loaded before the current one
+//     is converted, so its reads overlap this tile's conversion and stores;
+//   * column sums: per thread over its 8 rows in row order and over its tiles in tile order;
+//     then row blocks 2w and 2w + 1 (lanes l and l + 32 of wave w), the even one first; then the
+//     16 waves in order: one partial per block and column, partial[slot][column];
+//   * before its last tile's stores, a block publishes its partials (agent-scope atomic stores,
+//     coherent across the XCDs' L2 caches, complete before the next step) and adds one to its
+//     strip's counter (a relaxed agent-scope atomic add); the block that brings the count to
+//     nslots sums the strip's nslots partials in slot order into dbias (agent-scope atomic
+//     loads) and sets the counter back to zero.
+// The result does not depend on which block comes last, so it is the same run to run.  The
+// counters live at the start of the workspace: zero before the first call, and every call
+// leaves them zero.  Measured on the same buffers at [8192, 4096], cold: 24.7 us (68% of
+// 8 TB/s) against 29.1 us for the tile kernel + reduction, 27.2 us for this kernel with the
+// reduction as a second launch, 27.5 us for one-tile blocks at two blocks per CU.
+// ------------------------------------------------------------------------------------------
+constexpr int kStripBlocks = 256;                      // one 1024-thread block per CU
+constexpr int64_t kStripCounterBytes = 1024;           // counters for up to 256 strips
+constexpr int kMaxStrips = (int)(kStripCounterBytes / 4);
+static_assert(kStripCounterBytes == (int64_t)FP8DS_DBIAS_COUNTER_BYTES, "header and library agree");
+
+// Slots per strip for the one-launch form, or 0 when the tensor takes the two-kernel form.
+static int dbias_strip_slots(int64_t rows, int64_t cols) {
+    if (rows <= 0 || cols <= 0 || rows % kTile != 0 || cols % kTileC != 0) return 0;
+    const int64_t tiles_r = rows / kTile, tiles_c = cols / kTileC;
+    if (tiles_c > kMaxStrips || tiles_r * tiles_c > 2 * kStripBlocks) return 0;
+    const int64_t ns = std::min<int64_t>(tiles_r, kStripBlocks / tiles_c);
+    if (ns < 1 || 2 * ns < tiles_r) return 0;          // at most two tiles per block
+    return (int)ns;
+}
+
+// Row-by-row conversion of a thread's 8 x 8 micro-tile: amax, column sums and codes.  The sums
+// are pinned row by row (left to itself the compiler sinks them past the loop and keeps all 64
+// unpacked values live).  The rare exact path (a non-finite input, or a zero / non-finite
+// scale) reads the rows again.
+template <int FMT>
+__device__ __forceinline__ void strip_convert(const uint32_t (&w)[8][4], float s, const uint16_t *__restrict__ xr,
+                                              int64_t cols, uint32_t &mag, float (&cs)[8], uint32_t (&orow)[8][2]) {
+    uint32_t tam = 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) tam = amax_pk(tam, w[r][c]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            cs[2 * c] += bf16_lo(w[r][c]);
+            cs[2 * c + 1] += bf16_hi(w[r][c]);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) __asm__ volatile("" : "+v"(cs[k]));
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            orow[r][h] = pack4<FMT>(clamp_fmt<FMT>(bf16_lo(w[r][2 * h]) * s), clamp_fmt<FMT>(bf16_hi(w[r][2 * h]) * s),
+                                    clamp_fmt<FMT>(bf16_lo(w[r][2 * h + 1]) * s),
+                                    clamp_fmt<FMT>(bf16_hi(w[r][2 * h + 1]) * s));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const uint32_t m = amax_unpack(tam);
+    mag = max(mag, m);
+    if (!(scale_is_plain(s) && m < 0x7F80u)) {
+#pragma unroll 1
+        for (int r = 0; r < 8; ++r) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(xr + r * cols);
+            const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                orow[r][h] = encode_exact<FMT>(bf16_lo(q[2 * h]) * s) | (encode_exact<FMT>(bf16_hi(q[2 * h]) * s) << 8) |
+                             (encode_exact<FMT>(bf16_lo(q[2 * h + 1]) * s) << 16) |
+                             (encode_exact<FMT>(bf16_hi(q[2 * h + 1]) * s) << 24);
+        }
+    }
+}
+
+// Codes of one whole tile to out (row-major) and, through the LDS tile T[col][row], to out_t.
+__device__ __forceinline__ void strip_store(const uint32_t (&orow)[8][2], int64_t rows, int64_t cols, int64_t r0,
+                                            int64_t c0, int rb, int cb, int t, uint8_t *tT,
+                                            uint8_t *__restrict__ out, uint8_t *__restrict__ out_t) {
+    const int64_t row = r0 + rb * 8, col = c0 + cb * 8;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        u32x2 v = {orow[r][0], orow[r][1]};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(out + (row + r) * cols + col));
+    }
+    uint32_t ocol[8][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        tr4(orow[0][h], orow[1][h], orow[2][h], orow[3][h], ocol[4 * h][0], ocol[4 * h + 1][0], ocol[4 * h + 2][0],
+            ocol[4 * h + 3][0]);
+        tr4(orow[4][h], orow[5][h], orow[6][h], orow[7][h], ocol[4 * h][1], ocol[4 * h + 1][1], ocol[4 * h + 2][1],
+            ocol[4 * h + 3][1]);
+    }
+    __syncthreads();   // the previous tile's transposed reads are done
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int tc = cb * 8 + c;
+        u32x2 v = {ocol[c][0], ocol[c][1]};
+        *reinterpret_cast<u32x2 *>(&tT[tc * kTile + ((rb ^ t_swz(tc)) << 3)]) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < (kTileC * kTile / 16) / kCtThreads; ++i) {
+        const int q = t + kCtThreads * i;
+        const int tr = q >> 4, part = q & 15;
+        const int g = t_swz(tr);
+        u32x4 v = *reinterpret_cast<const u32x4 *>(&tT[tr * kTile + ((part ^ (g >> 1)) << 4)]);
+        if (g & 1) v = v.zwxy;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(out_t + (c0 + tr) * rows + r0 + part * 16));
+    }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kCtThreads) void k_dbias_strips(const uint16_t *__restrict__ x, int64_t rows,
+                                                             int64_t cols, const float *__restrict__ scale_p,
+                                                             uint8_t *__restrict__ out, uint8_t *__restrict__ out_t,
+                                                             float *sinv_out, float *amax_slot, float *partial,
+                                                             uint32_t *counters, float *__restrict__ dbias,
+                                                             int nslots) {
+    __shared__ __align__(16) uint8_t tT[kTileC * kTile];
+    __shared__ __align__(16) float csl[(kCtThreads / 64) * kTileC];
+    __shared__ uint32_t red[kCtThreads / 64];
+    __shared__ int last;
+    const float s = *scale_p;
+    const int t = threadIdx.x, rb = t >> 5, cb = t & 31, lane = t & 63, wave = t >> 6;
+    const int tiles_r = (int)(rows / kTile), tiles_c = (int)(cols / kTileC);
+    const int strip = (int)blockIdx.x % tiles_c, slot = (int)blockIdx.x / tiles_c;
+    const int64_t c0 = (int64_t)strip * kTileC, col = c0 + cb * 8;
+    uint32_t mag = 0;
+    float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    uint32_t w[8][4];
+    {
+        const uint16_t *xr = x + ((int64_t)slot * kTile + rb * 8) * cols + col;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xr + r * cols));
+            w[r][0] = v.x; w[r][1] = v.y; w[r][2] = v.z; w[r][3] = v.w;
+        }
+    }
+    for (int tr = slot; tr < tiles_r; tr += nslots) {
+        const int nx = tr + nslots;   // block-uniform
+        const uint16_t *xr = x + ((int64_t)tr * kTile + rb * 8) * cols + col;
+        uint32_t cur[8][4];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) cur[r][c] = w[r][c];
+        if (nx < tiles_r) {
+            const uint16_t *xn = x + ((int64_t)nx * kTile + rb * 8) * cols + col;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xn + r * cols));
+                w[r][0] = v.x; w[r][1] = v.y; w[r][2] = v.z; w[r][3] = v.w;
+            }
+        }
+        uint32_t orow[8][2];
+        strip_convert<FMT>(cur, s, xr, cols, mag, cs, orow);
+        if (nx >= tiles_r) {
+            // last tile of this block: publish the block's column sums and arrive on the strip
+            float o[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) o[k] = __shfl_xor(cs[k], 32);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) cs[k] = lane < 32 ? cs[k] + o[k] : o[k] + cs[k];
+            if (lane < 32) {
+                *reinterpret_cast<float4 *>(&csl[wave * kTileC + cb * 8]) = float4{cs[0], cs[1], cs[2], cs[3]};
+                *reinterpret_cast<float4 *>(&csl[wave * kTileC + cb * 8 + 4]) = float4{cs[4], cs[5], cs[6], cs[7]};
+            }
+            __syncthreads();
+            if (t < kTileC) {
+                float acc = 0.f;
+#pragma unroll
+                for (int wv = 0; wv < kCtThreads / 64; ++wv) acc += csl[wv * kTileC + t];
+                __hip_atomic_store(&partial[(int64_t)slot * cols + c0 + t], acc, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                // the partial has reached the coherent level before the arrival below
+                __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            __syncthreads();
+            if (t == 0) {
+                const uint32_t before =
+                    __hip_atomic_fetch_add(&counters[strip], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                last = before == (uint32_t)(nslots - 1);
+            }
+        }
+        strip_store(orow, rows, cols, (int64_t)tr * kTile, c0, rb, cb, t, tT, out, out_t);
+    }
+    __syncthreads();   // `last` is visible to every wave
+    if (last) {
+        if (t < kTileC) {
+            const float *p = partial + c0 + t;
+            float acc = 0.f;
+            for (int i = 0; i < nslots; i += 16) {
+                float v[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    v[u] = i + u < nslots ? __hip_atomic_load(p + (int64_t)(i + u) * cols, __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_AGENT)
+                                          : 0.f;
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    if (i + u < nslots) acc += v[u];
+            }
+            dbias[c0 + t] = acc;
+        }
+        if (t == 0) __hip_atomic_store(&counters[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const uint32_t bm = block_max_u32<kCtThreads>(mag, red);
+    if (t == 0) {
+        fold_amax(amax_slot, bm);
+        if (blockIdx.x == 0 && sinv_out != nullptr) *sinv_out = 1.0f / s;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------------
 hipError_t launch_cast_amax(const uint16_t *x, int64_t n, const float *scale, int fmt, uint8_t *out,
@@ -492,9 +715,11 @@ hipError_t launch_cast_transpose_pair(const uint16_t *x0, int64_t rows0, int64_t
     return launch_batch<false>(b, n0 + n1, v0, fmt, nullptr, st);
 }
 
+// Workspace: the strip counters of the one-launch form (kStripCounterBytes, zero between
+// calls), then the partial column sums, one row of cols floats per 256-row tile.
 size_t dbias_workspace_bytes(int64_t rows, int64_t cols) {
     if (rows <= 0 || cols <= 0) return 0;
-    return (size_t)((rows + kTile - 1) / kTile) * (size_t)cols * sizeof(float);
+    return (size_t)kStripCounterBytes + (size_t)((rows + kTile - 1) / kTile) * (size_t)cols * sizeof(float);
 }
 
 hipError_t launch_dbias_cast_transpose(const uint16_t *dy, int64_t rows, int64_t cols, const float *scale,
@@ -507,7 +732,18 @@ hipError_t launch_dbias_cast_transpose(const uint16_t *dy, int64_t rows, int64_t
         k_dbias_reduce<<<dim3((unsigned)((cols + 63) / 64)), dim3(256), 0, st>>>(nullptr, 0, cols, dbias);
         return hipGetLastError();
     }
-    float *partial = static_cast<float *>(ws);
+    uint32_t *counters = static_cast<uint32_t *>(ws);
+    float *partial = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + kStripCounterBytes);
+    if (const int nslots = dbias_strip_slots(rows, cols)) {
+        const unsigned grid = (unsigned)(nslots * (cols / kTileC));
+        if (fmt == kE4M3)
+            k_dbias_strips<kE4M3><<<dim3(grid), dim3(kCtThreads), 0, st>>>(dy, rows, cols, scale, out, out_t, sinv_out,
+                                                                          amax_slot, partial, counters, dbias, nslots);
+        else
+            k_dbias_strips<kE5M2><<<dim3(grid), dim3(kCtThreads), 0, st>>>(dy, rows, cols, scale, out, out_t, sinv_out,
+                                                                          amax_slot, partial, counters, dbias, nslots);
+        return hipGetLastError();
+    }
     hipError_t e = launch_ct<true>(dy, rows, cols, scale, fmt, out, out_t, sinv_out, amax_slot, nullptr, partial, st);
     if (e != hipSuccess) return e;
     const int64_t ntiles = (rows + kTile - 1) / kTile;

@@ -6,8 +6,9 @@
 // kNoallocScratchBytes instead, so the caller passes only inputs and outputs.  Each GPU the
 // library runs on holds its own copy of the array until the process ends.  Every call on a GPU
 // uses that GPU's one array: calls that overlap in time on one GPU (two streams, or two host
-// threads) race on it.  The partials are fully written before they are read within a call, so
-// nothing needs clearing between calls.
+// threads) race on it.  The partials are fully written before they are read within a call; the
+// strip counters at the start of the array are zero when the library is loaded (static storage)
+// and every call leaves them zero, so nothing needs clearing between calls.
 //
 // The array's name is only a host-side stand-in in host code; its device address comes from
 // hipGetSymbolAddress, taken once per device with that device current, and is what the kernels

@@ -107,8 +107,10 @@ int fp8_cast_transpose(const uint16_t *x, int64_t rows, int64_t cols, const floa
 
 /*
  * fp8_dbias_workspace_bytes -- HOST-only: workspace size fp8_dbias_cast_transpose needs for
- * a [rows, cols] dy (partial column sums of fixed-order row blocks).  0 for empty inputs.
+ * a [rows, cols] dy: FP8DS_DBIAS_COUNTER_BYTES of per-strip arrival counters, then the partial
+ * column sums of fixed-order row blocks (ceil(rows / 256) * cols float32).  0 for empty inputs.
  */
+#define FP8DS_DBIAS_COUNTER_BYTES ((size_t)1024)
 size_t fp8_dbias_workspace_bytes(int64_t rows, int64_t cols);
 
 /*
@@ -121,7 +123,13 @@ size_t fp8_dbias_workspace_bytes(int64_t rows, int64_t cols);
  *   out, out_t, amax, scale_inv as fp8_cast_transpose (E5M2 is the usual format for dy).
  *
  * dbias: [cols] float32.  workspace: at least fp8_dbias_workspace_bytes(rows, cols) bytes of
- * device scratch, contents on entry ignored.  No noop flag (dy is new every iteration).
+ * device memory, 4-byte aligned.  Its first FP8DS_DBIAS_COUNTER_BYTES must be zero before the
+ * first call that uses it (zero-fill a new workspace once, e.g. hipMemset after allocating
+ * it); every call leaves them zero again, so the workspace stays valid for later calls and
+ * graph replays of any shape.  The rest of it needs no initialisation.  Calls that overlap in
+ * time must not share a workspace.  Tensors of whole 256 x 256 tiles that give each CU at most
+ * two tiles run as one launch that finishes dbias itself (through those counters); all others
+ * as the tile kernel plus a reduction launch.  No noop flag (dy is new every iteration).
  */
 int fp8_dbias_cast_transpose(const uint16_t *dy, int64_t rows, int64_t cols, const float *scale,
                              int fmt, uint8_t *out, uint8_t *out_t, float *scale_inv_out,
@@ -134,11 +142,12 @@ int fp8_dbias_cast_transpose(const uint16_t *dy, int64_t rows, int64_t cols, con
  * harnesses that forbid allocation).  Same arguments, results and kernels, minus the
  * workspace: the partial column sums go to a static device array of
  * FP8DS_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on until the process
- * ends.  Calls nothing that allocates.  Limit: fp8_dbias_workspace_bytes(rows, cols) <=
- * FP8DS_NOALLOC_SCRATCH_BYTES (8 MiB: e.g. [8192, 16384] needs 2 MiB, [8192, 65536] 8 MiB),
- * else FP8DS_ERR_SCRATCH and nothing is launched.  All calls on one GPU share its array and
- * each call overwrites it, so calls that overlap in time on one GPU (on two streams, or from
- * two host threads) race: serialise them.
+ * ends (zero when the library is loaded, so its counters start at zero).  Calls nothing that
+ * allocates.  Limit: fp8_dbias_workspace_bytes(rows, cols) <= FP8DS_NOALLOC_SCRATCH_BYTES
+ * (8 MiB: e.g. [8192, 16384] needs 2 MiB + 1 KiB, and 8192 rows fit up to cols = 65528), else
+ * FP8DS_ERR_SCRATCH and nothing is launched.  All calls on one GPU share its array and each
+ * call overwrites it, so calls that overlap in time on one GPU (on two streams, or from two
+ * host threads) race: serialise them.
  */
 #define FP8DS_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
 int fp8_dbias_cast_transpose_noalloc(const uint16_t *dy, int64_t rows, int64_t cols,

@@ -61,7 +61,7 @@ def test_cast_validation():
 def test_dbias_validation():
     L = F.lib()
     need = F.fp8_dbias_workspace_bytes(300, 100)
-    assert need == 2 * 100 * 4       # one float per (256-row block, column)
+    assert need == 1024 + 2 * 100 * 4       # strip counters, then one float per (256-row block, column)
     assert F.fp8_dbias_workspace_bytes(0, 100) == 0
     assert L.fp8_dbias_cast_transpose(A16, 300, 100, A16, 1, A16, A16, None, None, A16, None, 0, None) == -5
     assert L.fp8_dbias_cast_transpose(A16, 300, 100, A16, 1, A16, A16, None, None, A16, A16, need - 4, None) == -5

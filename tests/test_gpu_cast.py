@@ -182,7 +182,7 @@ def test_dbias_cast_transpose_parity(shape):
     out = torch.empty((R, C), dtype=torch.uint8, device=DEV)
     out_t = torch.empty((C, R), dtype=torch.uint8, device=DEV)
     db = torch.full((C,), 7.0, dtype=torch.float32, device=DEV)
-    ws = torch.empty(F.fp8_dbias_workspace_bytes(R, C), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(F.fp8_dbias_workspace_bytes(R, C), dtype=torch.uint8, device=DEV)
     slot, sinv = scalar(0.0), scalar(0.0)
     scale = 4096.0
     F.fp8_dbias_cast_transpose(dy, scalar(scale), F.E5M2, out, out_t, db, ws, sinv, slot)
@@ -204,7 +204,7 @@ def test_dbias_constant_columns_exact(R):
     out = torch.empty((R, C), dtype=torch.uint8, device=DEV)
     out_t = torch.empty((C, R), dtype=torch.uint8, device=DEV)
     db = torch.empty((C,), dtype=torch.float32, device=DEV)
-    ws = torch.empty(F.fp8_dbias_workspace_bytes(R, C), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(F.fp8_dbias_workspace_bytes(R, C), dtype=torch.uint8, device=DEV)
     F.fp8_dbias_cast_transpose(dy, scalar(1.0), F.E5M2, out, out_t, db, ws)
     torch.cuda.synchronize()
     assert torch.all(db == R / 2)
@@ -216,7 +216,7 @@ def test_dbias_deterministic():
     dy = bf16_dev(dyh)
     out = torch.empty((R, C), dtype=torch.uint8, device=DEV)
     out_t = torch.empty((C, R), dtype=torch.uint8, device=DEV)
-    ws = torch.empty(F.fp8_dbias_workspace_bytes(R, C), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(F.fp8_dbias_workspace_bytes(R, C), dtype=torch.uint8, device=DEV)
     a = torch.empty((C,), dtype=torch.float32, device=DEV)
     b = torch.empty((C,), dtype=torch.float32, device=DEV)
     F.fp8_dbias_cast_transpose(dy, scalar(1.0), F.E5M2, out, out_t, a, ws)
@@ -225,10 +225,15 @@ def test_dbias_deterministic():
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
+COUNTER_BYTES = 1024   # FP8DS_DBIAS_COUNTER_BYTES: the strip counters at the start of the workspace
+
+
 @pytest.mark.parametrize("shape", [(2048, 1024), (300, 700), (8192, 4096)])
 def test_dbias_workspace_garbage_reuse_and_graph(shape):
-    """Whatever the workspace holds on entry (random bytes, all ones, zeros), dbias is the same
-    bits, call after call on the same workspace, and on every replay of a captured graph."""
+    """Whatever the partial-sum area holds on entry (random bytes, all ones, zeros), with the
+    counter bytes zero, dbias is the same bits, call after call on the same workspace, and on
+    every replay of a captured graph; every call leaves the counter bytes zero.  (2048, 1024) and
+    (8192, 4096) take the one-launch strip form, (300, 700) the tile kernel + reduction.)"""
     R, C = shape
     print(f"dbias workspace reuse {shape}", flush=True)
     dyh = S.normal_bf16(S.seed_for(3, 10), (R, C), 0.01)
@@ -236,22 +241,25 @@ def test_dbias_workspace_garbage_reuse_and_graph(shape):
     out = torch.empty((R, C), dtype=torch.uint8, device=DEV)
     out_t = torch.empty((C, R), dtype=torch.uint8, device=DEV)
     nbytes = F.fp8_dbias_workspace_bytes(R, C)
-    ws = torch.empty(nbytes + 64, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(nbytes + 64, dtype=torch.uint8, device=DEV)
     ref = torch.empty((C,), dtype=torch.float32, device=DEV)
     F.fp8_dbias_cast_transpose(dy, scalar(1.0), F.E5M2, out, out_t, ref, ws)
     torch.cuda.synchronize()
     db = oracle.dbias(dyh)
     assert np.all(np.abs(ref.cpu().numpy() - db) <= 1e-5 * np.abs(S.bf16_bits_to_f64(dyh)).sum(0) + 1e-30)
+    assert not torch.any(ws[:COUNTER_BYTES])
     fills = [torch.from_numpy(S.random_bytes(S.seed_for(3, 11), (nbytes + 64,))).to(DEV),
              torch.full((nbytes + 64,), 0xFF, dtype=torch.uint8, device=DEV),
              torch.zeros(nbytes + 64, dtype=torch.uint8, device=DEV)]
     for k, fill in enumerate(fills):
         ws.copy_(fill)
+        ws[:COUNTER_BYTES].zero_()
         for rep in range(3):
             got = torch.full((C,), float("nan"), dtype=torch.float32, device=DEV)
             F.fp8_dbias_cast_transpose(dy, scalar(1.0), F.E5M2, out, out_t, got, ws)
             torch.cuda.synchronize()
             assert torch.equal(got.view(torch.int32), ref.view(torch.int32)), (k, rep)
+            assert not torch.any(ws[:COUNTER_BYTES]), (k, rep)
     # captured once, replayed
     got = torch.zeros((C,), dtype=torch.float32, device=DEV)
     one = scalar(1.0)
@@ -266,6 +274,74 @@ def test_dbias_workspace_garbage_reuse_and_graph(shape):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(got.view(torch.int32), ref.view(torch.int32)), rep
+        assert not torch.any(ws[:COUNTER_BYTES]), rep
+
+
+# Shapes of whole 256 x 256 tiles that take the one-launch strip form: one tile per block
+# ([256, 256], [768, 512], [4096, 4096]), two per block ([8192, 4096]; [2560, 12288]: 48 strips x
+# 5 slots = 240 blocks for 10 row tiles; [512, 65536]: 256 strips, every counter in use).
+@pytest.mark.parametrize("shape", [(256, 256), (768, 512), (4096, 4096), (2560, 12288), (512, 65536)])
+def test_dbias_strip_form_parity(shape):
+    print(f"dbias strip form {shape}", flush=True)
+    R, C = shape
+    dyh = S.normal_bf16(S.seed_for(3, 40 + R % 7), shape, 0.01)
+    dy = bf16_dev(dyh)
+    out = torch.full((R, C), 0xA5, dtype=torch.uint8, device=DEV)
+    out_t = torch.full((C, R), 0x5A, dtype=torch.uint8, device=DEV)
+    db = torch.full((C,), float("nan"), dtype=torch.float32, device=DEV)
+    ws = torch.zeros(F.fp8_dbias_workspace_bytes(R, C), dtype=torch.uint8, device=DEV)
+    slot, sinv = scalar(0.0), scalar(0.0)
+    F.fp8_dbias_cast_transpose(dy, scalar(4096.0), F.E5M2, out, out_t, db, ws, sinv, slot)
+    torch.cuda.synchronize()
+    rq, rqt, ra, rs, rdb = oracle.dbias_cast_transpose(dyh, 4096.0, F.E5M2)
+    assert np.array_equal(u8_host(out), rq) and np.array_equal(u8_host(out_t), rqt)
+    assert f32_bits(slot.item()) == f32_bits(ra) and f32_bits(sinv.item()) == f32_bits(rs)
+    assert np.all(np.abs(db.cpu().numpy().astype(np.float64) - rdb) <= _dbias_bound(dyh))
+    assert not torch.any(ws[:COUNTER_BYTES])
+
+
+@pytest.mark.parametrize("scale", [2.0 ** 10, 0.0, float("inf")])
+def test_dbias_strip_form_specials(scale):
+    """Infinities, NaNs and saturating values in a strip-form tensor, and scales that are not
+    plain (zero, infinite): the exact path re-reads the rows; codes, amax and inverse scale
+    must equal the oracle's; dbias is checked where the column holds no non-finite value."""
+    R, C = 1024, 512
+    dyh = S.normal_bf16(S.seed_for(3, 50), (R, C), 1.0)
+    for (i, j, v) in [(3, 5, 0x7F80), (700, 5, 0xFF80), (511, 300, 0x7FC0), (1023, 511, 0x7F7F), (9, 0, 0xFF7F),
+                      (256, 256, 0x4780)]:
+        dyh[i, j] = v
+    dy = bf16_dev(dyh)
+    out = torch.empty((R, C), dtype=torch.uint8, device=DEV)
+    out_t = torch.empty((C, R), dtype=torch.uint8, device=DEV)
+    db = torch.empty((C,), dtype=torch.float32, device=DEV)
+    ws = torch.zeros(F.fp8_dbias_workspace_bytes(R, C), dtype=torch.uint8, device=DEV)
+    slot, sinv = scalar(0.0), scalar(0.0)
+    F.fp8_dbias_cast_transpose(dy, scalar(scale), F.E5M2, out, out_t, db, ws, sinv, slot)
+    torch.cuda.synchronize()
+    rq, rqt, ra, rs, rdb = oracle.dbias_cast_transpose(dyh, scale, F.E5M2)
+    assert np.array_equal(u8_host(out), rq) and np.array_equal(u8_host(out_t), rqt)
+    assert f32_bits(slot.item()) == f32_bits(ra) and f32_bits(sinv.item()) == f32_bits(rs)
+    got = db.cpu().numpy().astype(np.float64)
+    finite = np.all(np.isfinite(S.bf16_bits_to_f64(dyh)), axis=0)
+    assert np.all(np.abs(got[finite] - rdb[finite]) <= _dbias_bound(dyh)[finite])
+    assert not torch.any(ws[:COUNTER_BYTES])
+
+
+def test_dbias_workspace_shared_by_both_forms():
+    """One workspace used in turn by a strip-form shape and a tile-kernel shape, new data every
+    call: each call's dbias matches the oracle (no partial or counter left by the other form)."""
+    ws = torch.zeros(F.fp8_dbias_workspace_bytes(2048, 1024), dtype=torch.uint8, device=DEV)
+    for k, (R, C) in enumerate([(2048, 1024), (300, 700), (2048, 1024), (1000, 1024), (512, 512)]):
+        print(f"dbias shared workspace call {k} {(R, C)}", flush=True)
+        assert F.fp8_dbias_workspace_bytes(R, C) <= ws.numel()
+        dyh = S.normal_bf16(S.seed_for(3, 60 + k), (R, C), 0.01)
+        out = torch.empty((R, C), dtype=torch.uint8, device=DEV)
+        out_t = torch.empty((C, R), dtype=torch.uint8, device=DEV)
+        db = torch.full((C,), float("nan"), dtype=torch.float32, device=DEV)
+        F.fp8_dbias_cast_transpose(bf16_dev(dyh), scalar(1.0), F.E5M2, out, out_t, db, ws)
+        torch.cuda.synchronize()
+        assert np.all(np.abs(db.cpu().numpy().astype(np.float64) - oracle.dbias(dyh)) <= _dbias_bound(dyh)), k
+        assert not torch.any(ws[:COUNTER_BYTES]), k
 
 
 def test_empty_inputs_launch_nothing():

@@ -45,7 +45,7 @@ def step():
     dx = torch.empty((M, K), device=DEV, dtype=torch.bfloat16)
     dw = torch.empty((N, K), **f32)
     db = torch.empty(N, **f32)
-    ws = torch.empty(F.fp8_dbias_workspace_bytes(M, N), **u8)
+    ws = torch.zeros(F.fp8_dbias_workspace_bytes(M, N), **u8)
     print("full-size QKV step: fwd + bwd on the GPU", flush=True)
     F.fp8_linear_fwd(bf16_dev(xh), bf16_dev(wh), bf16_dev(bh), scale[0:1], hist[0, 0:1], x8, x8t, sinv[0:1],
                      scale[1:2], hist[0, 1:2], w8, w8t, sinv[1:2], None, y)

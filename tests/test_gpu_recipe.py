@@ -157,7 +157,7 @@ class Layer:
         self.dx = torch.empty((M, K), device=DEV, dtype=torch.bfloat16)
         self.dw = torch.empty((N, K), device=DEV, dtype=torch.float32 if dw_fp32 else torch.bfloat16)
         self.db = torch.empty(N, **f32)
-        self.ws = torch.empty(max(1, F.fp8_dbias_workspace_bytes(M, N)), **u8)
+        self.ws = torch.zeros(max(1, F.fp8_dbias_workspace_bytes(M, N)), **u8)
         self.noop = torch.zeros(1, **f32)
 
     def fwd(self, x, w, b, stream=None, noop=None):
@@ -236,7 +236,7 @@ def test_linear_equals_primitive_sequence():
     y = torch.empty((M, N), device=DEV, dtype=torch.bfloat16)
     F.fp8_gemm_bias(x8, F.E4M3, sinv[0:1], w8, F.E4M3, sinv[1:2], b, y)
     db = torch.empty(N, device=DEV)
-    ws = torch.empty(F.fp8_dbias_workspace_bytes(M, N), **u8)
+    ws = torch.zeros(F.fp8_dbias_workspace_bytes(M, N), **u8)
     F.fp8_dbias_cast_transpose(dy, lay.scale[2:3], F.E5M2, dy8, dy8t, db, ws, sinv[2:3], am[2:3])
     dx = torch.empty((M, K), device=DEV, dtype=torch.bfloat16)
     dw = torch.empty((N, K), device=DEV, dtype=torch.float32)

@@ -48,7 +48,7 @@ def _one(shape, seed):
     assert st == 0, F.fp8ds_status_string(st)
     # the existing entry point with its own workspace
     rout, rout_t, rdb, rslot, rsinv = _outputs(R, C)
-    ws = torch.empty(F.fp8_dbias_workspace_bytes(R, C), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(F.fp8_dbias_workspace_bytes(R, C), dtype=torch.uint8, device=DEV)
     F.fp8_dbias_cast_transpose(dy, scale, F.E5M2, rout, rout_t, rdb, ws, rsinv, rslot)
     torch.cuda.synchronize()
     assert torch.equal(out, rout) and torch.equal(out_t, rout_t)
