@@ -459,7 +459,7 @@ def extras(F, S, torch, np, dev, bf16, step):
 
     out.update(cast_family(F, S, torch, np, dev, bf16))
 
-    # small forward layer: eager call vs graph replay
+    # small forward layer: eager call vs graph replay (one launch: the casts run inside the GEMM kernel)
     Ms, Ns, Ks = 128, 256, 256
     xs, wsm, bs = bf16(S.normal_bf16(S.seed_for(0, 0), (Ms, Ks), 1.0)), bf16(S.normal_bf16(S.seed_for(0, 1), (Ns, Ks), 1.0)), \
         bf16(S.normal_bf16(S.seed_for(0, 2), (Ns,), 0.1))
@@ -503,7 +503,7 @@ def extras(F, S, torch, np, dev, bf16, step):
     torch.cuda.synchronize()
     raw_us = (time.perf_counter() - t) / 200 * 1e6
     out["small_forward_128x256x256"] = {"eager_us_per_call": round(eager_us, 2), "graph_replay_us": round(graph_us, 2),
-                                        "c_abi_eager_us_per_call": round(raw_us, 2), "launches": 2}
+                                        "c_abi_eager_us_per_call": round(raw_us, 2), "launches": 1}
 
     # N-chunked GEMM + bias, M=8192, K=N=12288 (x8 and the first 12288 rows of W8), one stream
     # per chunk, captured as one graph

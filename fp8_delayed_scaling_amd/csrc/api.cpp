@@ -277,6 +277,9 @@ int fp8_linear_fwd(const uint16_t *x, const uint16_t *w, const uint16_t *bias, i
     st = check_gemm(x8, FP8DS_E4M3, x_scale_inv, K, w8, FP8DS_E4M3, w_scale_inv, K, bias, y, N, FP8DS_OUT_BF16, M,
                     N, K);
     if (st != FP8DS_OK) return st;
+    if (fp8ds::linear_fwd_small_ok(M, N, K, x8_t))
+        return hip_status(fp8ds::launch_linear_fwd_small(x, w, bias, M, N, K, x_scale, x_amax, x8, x_scale_inv,
+                                                         w_scale, w_amax, w8, w8_t, w_scale_inv, w_noop, y, stream));
     if (K > 0) {
         // x (with or without its transpose) and W in one launch
         hipError_t e = fp8ds::launch_cast_transpose_pair(x, M, K, x_scale, x8, x8_t, x_scale_inv, x_amax, nullptr,

@@ -1172,6 +1172,192 @@ __global__ __launch_bounds__(64) void k_gemm_small16(const uint8_t *__restrict__
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// k_linear_fwd_small: the forward of a small FP8 linear layer in one launch.  At the size of a
+// [128, 256] x [256, 256] layer both kernels of the two-launch form are pure latency (a cast
+// launch of two tiles, then eight waves of GEMM), so here each 64 x 64 output tile's block casts
+// the bfloat16 rows it multiplies itself: per 128-byte K step, wave w casts x rows 16 w .. and W
+// rows 16 w .. of the tile in registers (the x fragment feeds its own MFMAs; the W fragments are
+// exchanged through a 64 x 128-byte LDS tile), and the MFMAs run in the K order of
+// k_gemm_small16 on the same fragments, so y is identical.  The casts' outputs are written by
+// the blocks that own them: tile column 0 writes x8 and folds x's amax; tile row 0 writes w8,
+// folds W's amax and writes w8_t from the LDS tile.  A cached weight (*w_noop == 1) is read as
+// codes from w8 and nothing of W is written.  Every code equals the cast kernels' (same clamp +
+// hardware conversion, the exact encoder for a fragment holding an inf / NaN or under a zero /
+// non-finite scale), and 1/scale is formed as the cast kernels form it.
+// ------------------------------------------------------------------------------------------
+struct SmallFwdArgs {
+    const uint16_t *x, *w, *bias;
+    const float *x_scale, *w_scale, *w_noop;
+    float *x_amax, *w_amax, *x_scale_inv, *w_scale_inv;
+    uint8_t *x8, *w8, *w8_t;
+    uint16_t *y;
+    int M, N, K, tiles_n;
+};
+
+// 32 bfloat16 values (16 dwords, element 2q in the low half of dword q) -> 32 E4M3 codes
+// (8 dwords, element 4d in byte 0 of dword d); *tam receives the packed magnitudes' max.
+__device__ __forceinline__ i32x8 cast32_e4m3(const uint32_t (&v)[16], float s, bool plain, uint32_t *tam) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) m = amax_pk(m, v[q]);
+    *tam = m;
+    i32x8 r;
+    if (plain && amax_unpack(m) < 0x7F80u) {
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+            r[d] = (int)pack4<kE4M3>(clamp_fmt<kE4M3>(bf16_lo(v[2 * d]) * s), clamp_fmt<kE4M3>(bf16_hi(v[2 * d]) * s),
+                                     clamp_fmt<kE4M3>(bf16_lo(v[2 * d + 1]) * s),
+                                     clamp_fmt<kE4M3>(bf16_hi(v[2 * d + 1]) * s));
+    } else {
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+            r[d] = (int)(encode_exact<kE4M3>(bf16_lo(v[2 * d]) * s) | (encode_exact<kE4M3>(bf16_hi(v[2 * d]) * s) << 8) |
+                         (encode_exact<kE4M3>(bf16_lo(v[2 * d + 1]) * s) << 16) |
+                         (encode_exact<kE4M3>(bf16_hi(v[2 * d + 1]) * s) << 24));
+    }
+    return r;
+}
+
+__device__ __forceinline__ void load32_bf16(const uint16_t *p, uint32_t (&v)[16]) {
+    const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const u32x4 t = q[c];
+        v[4 * c] = t.x; v[4 * c + 1] = t.y; v[4 * c + 2] = t.z; v[4 * c + 3] = t.w;
+    }
+}
+
+__device__ __forceinline__ void store32_codes(uint8_t *p, const i32x8 &c) {
+    reinterpret_cast<u32x4 *>(p)[0] = u32x4{(uint32_t)c[0], (uint32_t)c[1], (uint32_t)c[2], (uint32_t)c[3]};
+    reinterpret_cast<u32x4 *>(p)[1] = u32x4{(uint32_t)c[4], (uint32_t)c[5], (uint32_t)c[6], (uint32_t)c[7]};
+}
+
+__global__ __launch_bounds__(256) void k_linear_fwd_small(const SmallFwdArgs a) {
+    __shared__ __align__(16) uint8_t sw[kSmallTile * kQK];   // the tile's W codes of one K step: [row][k]
+    const int tm = blockIdx.x / a.tiles_n, tn = blockIdx.x - (blockIdx.x / a.tiles_n) * a.tiles_n;
+    const int m0 = tm * kSmallTile, n0 = tn * kSmallTile;
+    const int t = threadIdx.x, lane = t & 63, r16 = lane & 15, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // 16-row slice of x and of W
+    const int M = a.M, N = a.N, K = a.K;
+    const float xs = *a.x_scale;
+    const bool wcached = a.w_noop != nullptr && *a.w_noop == 1.0f;
+    const float ws = *a.w_scale;
+    const float sa = 1.0f / xs;
+    const float sb = wcached ? *a.w_scale_inv : 1.0f / ws;
+    if (blockIdx.x == 0 && t == 0) {
+        *a.x_scale_inv = sa;
+        if (!wcached) *a.w_scale_inv = sb;
+    }
+    const bool own_x = tn == 0, own_w = tm == 0 && !wcached;   // block-uniform
+    const bool plain_x = scale_is_plain(xs), plain_w = scale_is_plain(ws);
+    // lane l of wave w supplies row 16 w + l % 16 of the x and W tiles and K bytes
+    // [32 (l / 16), +32) of each 128-byte step; rows past M / N repeat the last row (never stored)
+    const int xrow = m0 + wave * 16 + r16, wrow = n0 + wave * 16 + r16;
+    const uint16_t *xsrc = a.x + (int64_t)min(xrow, M - 1) * K + g * 32;
+    const uint16_t *wsrc = a.w + (int64_t)min(wrow, N - 1) * K + g * 32;
+    const uint8_t *w8src = a.w8 + (int64_t)min(wrow, N - 1) * K + g * 32;
+    f32x4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool has_bias = a.bias != nullptr;
+    const uint16_t *bsrc = has_bias ? a.bias : reinterpret_cast<const uint16_t *>(a.x_scale);
+    uint32_t braw[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) braw[j][u] = bsrc[has_bias ? min(n0 + j * 16 + g * 4 + u, N - 1) : 0];
+    uint32_t xam = 0, wam = 0;
+    const int nk = K / kQK;
+    // the next step's rows are loaded before this step is cast (one step ahead)
+    uint32_t nx[16], nw[16] = {};
+    load32_bf16(xsrc, nx);
+    if (wcached) {
+        const u32x4 *q = reinterpret_cast<const u32x4 *>(w8src);
+        const u32x4 lo = q[0], hi = q[1];
+        nw[0] = lo.x; nw[1] = lo.y; nw[2] = lo.z; nw[3] = lo.w; nw[4] = hi.x; nw[5] = hi.y; nw[6] = hi.z; nw[7] = hi.w;
+    } else {
+        load32_bf16(wsrc, nw);
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const int kc = kt * kQK;
+        uint32_t vx[16], vw[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) { vx[q] = nx[q]; vw[q] = nw[q]; }
+        if (kt + 1 < nk) {
+            load32_bf16(xsrc + kc + kQK, nx);
+            if (wcached) {
+                const u32x4 *q = reinterpret_cast<const u32x4 *>(w8src + kc + kQK);
+                const u32x4 lo = q[0], hi = q[1];
+                nw[0] = lo.x; nw[1] = lo.y; nw[2] = lo.z; nw[3] = lo.w; nw[4] = hi.x; nw[5] = hi.y; nw[6] = hi.z; nw[7] = hi.w;
+            } else {
+                load32_bf16(wsrc + kc + kQK, nw);
+            }
+        }
+        i32x8 fbw;
+        if (wcached)
+            fbw = i32x8{(int)vw[0], (int)vw[1], (int)vw[2], (int)vw[3], (int)vw[4], (int)vw[5], (int)vw[6], (int)vw[7]};
+        uint32_t tam;
+        const i32x8 fa = cast32_e4m3(vx, xs, plain_x, &tam);
+        if (own_x) {
+            xam = amax_pk(xam, tam);
+            if (xrow < M) store32_codes(a.x8 + (int64_t)xrow * K + kc + g * 32, fa);
+        }
+        if (!wcached) {
+            fbw = cast32_e4m3(vw, ws, plain_w, &tam);
+            if (own_w) {
+                wam = amax_pk(wam, tam);
+                if (wrow < N) store32_codes(a.w8 + (int64_t)wrow * K + kc + g * 32, fbw);
+            }
+        }
+        if (kt > 0) __syncthreads();   // every wave has read the previous step's W codes
+        store32_codes(sw + (wave * 16 + r16) * kQK + g * 32, fbw);
+        __syncthreads();
+        if (own_w) {
+            // w8_t rows kc + k, columns n0 .. n0 + 63 = sw[.][k]: thread t gathers k = t / 2,
+            // columns 32 (t % 2) .. + 31
+            const int k = t >> 1, c0 = (t & 1) * 32;
+            uint32_t d[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                d[c] = (uint32_t)sw[(c0 + 4 * c) * kQK + k] | ((uint32_t)sw[(c0 + 4 * c + 1) * kQK + k] << 8) |
+                       ((uint32_t)sw[(c0 + 4 * c + 2) * kQK + k] << 16) | ((uint32_t)sw[(c0 + 4 * c + 3) * kQK + k] << 24);
+            uint8_t *dst = a.w8_t + (int64_t)(kc + k) * N + n0 + c0;
+            if (n0 + c0 < N) reinterpret_cast<u32x4 *>(dst)[0] = u32x4{d[0], d[1], d[2], d[3]};
+            if (n0 + c0 + 16 < N) reinterpret_cast<u32x4 *>(dst)[1] = u32x4{d[4], d[5], d[6], d[7]};
+        }
+        i32x8 fb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u32x4 *q = reinterpret_cast<const u32x4 *>(sw + (j * 16 + r16) * kQK + g * 32);
+            const u32x4 lo = q[0], hi = q[1];
+            fb[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], fa, acc[j], kE4M3, kE4M3, 0, 0, 0, 0);
+    }
+    // epilogue as k_gemm_small16 (bfloat16 out): lane l of wave w holds y[m0 + 16 w + l % 16]
+    // [n0 + 16 j + 4 (l / 16) + u] in element u of acc[j]
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int col = n0 + j * 16 + g * 4 + u;
+            const float b = has_bias ? __uint_as_float(braw[j][u] << 16) : 0.f;
+            const float val = dequant_bias(acc[j][u], sa, sb, b);
+            if (xrow < M && col < N) a.y[(int64_t)xrow * N + col] = f32_to_bf16_rne(val);
+        }
+    if (own_x) {
+        const uint32_t m = wave_max_u32(amax_unpack(xam));
+        if (lane == 0) fold_amax(a.x_amax, m);
+    }
+    if (own_w) {
+        const uint32_t m = wave_max_u32(amax_unpack(wam));
+        if (lane == 0) fold_amax(a.w_amax, m);
+    }
+}
+
 // D = bias broadcast (K == 0): no products at all.
 template <int OUT>
 __global__ __launch_bounds__(256) void k_bias_only(const uint16_t *__restrict__ bias, void *__restrict__ D,
@@ -1269,6 +1455,30 @@ hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64
     }
 #undef FP8DS_GEMM_OUT
 #undef FP8DS_GEMM
+    return hipGetLastError();
+}
+
+// The one-launch small forward applies when the GEMM takes the small 16 x 16 x 128 kernel
+// (K % 256 == 0, fewer than kSmallTiles tiles of 256 x 256), K <= 8192, N % 16 == 0 (whole
+// 16-byte chunks of w8_t rows) and x's transpose is not asked for.
+bool linear_fwd_small_ok(int64_t M, int64_t N, int64_t K, const uint8_t *x8_t) {
+    if (x8_t != nullptr || M <= 0 || N <= 0 || K <= 0 || K % kFam16K != 0 || K > 8192 || N % 16 != 0) return false;
+    return ((M + BM - 1) / BM) * ((N + BN - 1) / BN) < kSmallTiles;
+}
+
+hipError_t launch_linear_fwd_small(const uint16_t *x, const uint16_t *w, const uint16_t *bias, int64_t M, int64_t N,
+                                   int64_t K, const float *x_scale, float *x_amax, uint8_t *x8, float *x_scale_inv,
+                                   const float *w_scale, float *w_amax, uint8_t *w8, uint8_t *w8_t,
+                                   float *w_scale_inv, const float *w_noop, uint16_t *y, hipStream_t st) {
+    SmallFwdArgs a{};
+    a.x = x; a.w = w; a.bias = bias;
+    a.x_scale = x_scale; a.w_scale = w_scale; a.w_noop = w_noop;
+    a.x_amax = x_amax; a.w_amax = w_amax; a.x_scale_inv = x_scale_inv; a.w_scale_inv = w_scale_inv;
+    a.x8 = x8; a.w8 = w8; a.w8_t = w8_t; a.y = y;
+    a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    a.tiles_n = (int)((N + kSmallTile - 1) / kSmallTile);
+    const unsigned grid = (unsigned)(((M + kSmallTile - 1) / kSmallTile) * a.tiles_n);
+    k_linear_fwd_small<<<dim3(grid), dim3(256), 0, st>>>(a);
     return hipGetLastError();
 }
 

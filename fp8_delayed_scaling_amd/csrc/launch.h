@@ -37,4 +37,12 @@ hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64
                             int out_dtype, int64_t M, int64_t N, int64_t K, const float *d_scale,
                             float *d_sinv_out, float *d_amax, hipStream_t st);
 
+// The forward of a small layer (casts of x and W, GEMM + bias, bfloat16 y) in one launch, with
+// the results of the cast-pair launch + GEMM launch; linear_fwd_small_ok says when it applies.
+bool linear_fwd_small_ok(int64_t M, int64_t N, int64_t K, const uint8_t *x8_t);
+hipError_t launch_linear_fwd_small(const uint16_t *x, const uint16_t *w, const uint16_t *bias, int64_t M, int64_t N,
+                                   int64_t K, const float *x_scale, float *x_amax, uint8_t *x8, float *x_scale_inv,
+                                   const float *w_scale, float *w_amax, uint8_t *w8, uint8_t *w8_t,
+                                   float *w_scale_inv, const float *w_noop, uint16_t *y, hipStream_t st);
+
 }  // namespace fp8ds
