@@ -329,7 +329,10 @@ def fp8_linear_fwd(x, w, bias, x_scale, x_amax, x8, x8_t, x_scale_inv, w_scale, 
 
 def fp8_linear_bwd(dy, K, dy_scale, dy_amax, dy8, dy8_t, dy_scale_inv, dbias, workspace, x8_t, x_scale_inv, w8_t,
                    w_scale_inv, dx, dw, stream=None):
-    """Backward of the FP8 linear layer: dbias + cast+transpose of dy, dgrad and wgrad GEMMs."""
+    """Backward of the FP8 linear layer: dbias + cast+transpose of dy, dgrad and wgrad GEMMs.
+
+    ``workspace`` (with ``dbias``): zero-filled before its first use, as for
+    ``fp8_dbias_cast_transpose``."""
     _want(dy, _BF16, "dy", required=True)
     M, N = dy.shape
     K = int(K)

@@ -1140,31 +1140,56 @@ __global__ __launch_bounds__(64) void k_gemm_small16(const uint8_t *__restrict__
     if (kt + 1 < nk) { FP8DS_SMFMA(a1, b1) }
 #undef FP8DS_SLOAD
 #undef FP8DS_SMFMA
-    // epilogue, element by element: lane l holds D[m0 + 16 i + l % 16][n0 + 16 j + 4 (l / 16) + u]
-    // in element u of acc[i][j]
+    // epilogue: lane l holds D[m0 + 16 i + l % 16][n0 + 16 j + 4 (l / 16) + u] in element u of
+    // acc[i][j]; the four columns go out in one store when they are inside D and the store is
+    // aligned (4 x the element size), else element by element
+    constexpr int kEsz = OUT == 0 ? 2 : OUT == 1 ? 4 : 1;
+    const bool vec4 = ((reinterpret_cast<uintptr_t>(D) & (uintptr_t)(4 * kEsz - 1)) == 0) && (ldd % 4 == 0);
     uint32_t amag = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = m0 + i * 16 + r16;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
+            const int col = n0 + j * 16 + g * 4;
+            float v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int col = n0 + j * 16 + g * 4 + u;
                 const float b = has_bias ? __uint_as_float(braw[j][u] << 16) : 0.f;
-                const float v = dequant_bias(acc[i][j][u], sa, sb, b);
-                if (row < M && col < N) {
-                    const int64_t o = (int64_t)row * ldd + col;
+                v[u] = dequant_bias(acc[i][j][u], sa, sb, b);
+            }
+            if (row >= M) continue;
+            const int64_t o = (int64_t)row * ldd + col;
+            if constexpr (OUT >= 2) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (col + u < N) amag = max(amag, __float_as_uint(v[u]) & 0x7FFFFFFFu);
+            }
+            if (vec4 && col + 3 < N) {
+                if constexpr (OUT == 0) {
+                    *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(D) + o) =
+                        u32x2{f32x2_to_bf16x2_rne(v[0], v[1]), f32x2_to_bf16x2_rne(v[2], v[3])};
+                } else if constexpr (OUT == 1) {
+                    *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(D) + o) = f32x4{v[0], v[1], v[2], v[3]};
+                } else {
+                    *reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(D) + o) =
+                        encode_exact<OUT - 2>(v[0] * ds) | (encode_exact<OUT - 2>(v[1] * ds) << 8) |
+                        (encode_exact<OUT - 2>(v[2] * ds) << 16) | (encode_exact<OUT - 2>(v[3] * ds) << 24);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (col + u >= N) continue;
                     if constexpr (OUT == 0) {
-                        reinterpret_cast<uint16_t *>(D)[o] = f32_to_bf16_rne(v);
+                        reinterpret_cast<uint16_t *>(D)[o + u] = f32_to_bf16_rne(v[u]);
                     } else if constexpr (OUT == 1) {
-                        reinterpret_cast<float *>(D)[o] = v;
+                        reinterpret_cast<float *>(D)[o + u] = v[u];
                     } else {
-                        amag = max(amag, __float_as_uint(v) & 0x7FFFFFFFu);
-                        reinterpret_cast<uint8_t *>(D)[o] = (uint8_t)encode_exact<OUT - 2>(v * ds);
+                        reinterpret_cast<uint8_t *>(D)[o + u] = (uint8_t)encode_exact<OUT - 2>(v[u] * ds);
                     }
                 }
             }
+        }
     }
     if constexpr (OUT >= 2) {
         amag = wave_max_u32(amag);
@@ -1339,15 +1364,28 @@ __global__ __launch_bounds__(256) void k_linear_fwd_small(const SmallFwdArgs a) 
     }
     // epilogue as k_gemm_small16 (bfloat16 out): lane l of wave w holds y[m0 + 16 w + l % 16]
     // [n0 + 16 j + 4 (l / 16) + u] in element u of acc[j]
+    // (N % 16 == 0: a lane's four columns are all inside or all outside; one 8-byte store each
+    // when y is 8-byte aligned)
+    const bool y8 = (reinterpret_cast<uintptr_t>(a.y) & 7u) == 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+        const int col = n0 + j * 16 + g * 4;
+        float val[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int col = n0 + j * 16 + g * 4 + u;
             const float b = has_bias ? __uint_as_float(braw[j][u] << 16) : 0.f;
-            const float val = dequant_bias(acc[j][u], sa, sb, b);
-            if (xrow < M && col < N) a.y[(int64_t)xrow * N + col] = f32_to_bf16_rne(val);
+            val[u] = dequant_bias(acc[j][u], sa, sb, b);
         }
+        if (xrow < M && col < N) {
+            uint16_t *dst = a.y + (int64_t)xrow * N + col;
+            if (y8) {
+                *reinterpret_cast<u32x2 *>(dst) = u32x2{f32x2_to_bf16x2_rne(val[0], val[1]), f32x2_to_bf16x2_rne(val[2], val[3])};
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) dst[u] = f32_to_bf16_rne(val[u]);
+            }
+        }
+    }
     if (own_x) {
         const uint32_t m = wave_max_u32(amax_unpack(xam));
         if (lane == 0) fold_amax(a.x_amax, m);

@@ -292,7 +292,8 @@ int fp8_linear_fwd(const uint16_t *x, const uint16_t *w, const uint16_t *bias,
  *   3. wgrad dW[N, K] = gemm(dy8_t [N, M] E5M2, x8_t [K, M] E4M3), bfloat16 or float32.
  * dy: [M, N] bfloat16.  dbias: [N] float32 or NULL (then no bias gradient is formed and the
  * plain cast_transpose is used).  workspace: fp8_dbias_workspace_bytes(M, N) bytes when dbias
- * is given.  x8_t, w8_t and their inverse scales come from the forward.  M % 16 == 0 and
+ * is given, zero-filled before its first use as for fp8_dbias_cast_transpose (every call leaves
+ * its counters zero).  x8_t, w8_t and their inverse scales come from the forward.  M % 16 == 0 and
  * N % 16 == 0 (they are the contraction lengths of wgrad and dgrad).
  */
 int fp8_linear_bwd(const uint16_t *dy, int64_t M, int64_t N, int64_t K,

@@ -281,8 +281,9 @@ def test_dbias_workspace_garbage_reuse_and_graph(shape):
 # ([256, 256], [768, 512], [4096, 4096]), two per block ([8192, 4096]; [2560, 12288]: 48 strips x
 # 5 slots = 240 blocks for 10 row tiles; [512, 65536]: 256 strips, every counter in use).
 @pytest.mark.parametrize("shape", [(256, 256), (768, 512), (4096, 4096), (2560, 12288), (512, 65536)])
-def test_dbias_strip_form_parity(shape):
-    print(f"dbias strip form {shape}", flush=True)
+@pytest.mark.parametrize("fmt", [1, 0])
+def test_dbias_strip_form_parity(shape, fmt):
+    print(f"dbias strip form {shape} fmt {fmt}", flush=True)
     R, C = shape
     dyh = S.normal_bf16(S.seed_for(3, 40 + R % 7), shape, 0.01)
     dy = bf16_dev(dyh)
@@ -291,9 +292,10 @@ def test_dbias_strip_form_parity(shape):
     db = torch.full((C,), float("nan"), dtype=torch.float32, device=DEV)
     ws = torch.zeros(F.fp8_dbias_workspace_bytes(R, C), dtype=torch.uint8, device=DEV)
     slot, sinv = scalar(0.0), scalar(0.0)
-    F.fp8_dbias_cast_transpose(dy, scalar(4096.0), F.E5M2, out, out_t, db, ws, sinv, slot)
+    scale = 4096.0 if fmt == F.E5M2 else 64.0
+    F.fp8_dbias_cast_transpose(dy, scalar(scale), fmt, out, out_t, db, ws, sinv, slot)
     torch.cuda.synchronize()
-    rq, rqt, ra, rs, rdb = oracle.dbias_cast_transpose(dyh, 4096.0, F.E5M2)
+    rq, rqt, ra, rs, rdb = oracle.dbias_cast_transpose(dyh, scale, fmt)
     assert np.array_equal(u8_host(out), rq) and np.array_equal(u8_host(out_t), rqt)
     assert f32_bits(slot.item()) == f32_bits(ra) and f32_bits(sinv.item()) == f32_bits(rs)
     assert np.all(np.abs(db.cpu().numpy().astype(np.float64) - rdb) <= _dbias_bound(dyh))
