@@ -33,6 +33,7 @@ kernel's own duration (comparable with a profiler's kernel trace).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -365,6 +366,21 @@ def cold_rotating(torch, calls, bytes_per_call, reps=5):
     return s.elapsed_time(e) / (reps * len(calls))
 
 
+def _abi(F, torch, name, *args):
+    """One call of a C-ABI entry point with its arguments marshalled once (tensors as device
+    addresses, the current stream last): what a C caller pays per call, without the Python
+    binding's checks, so short kernels are timed rather than the host."""
+    fn = getattr(F.lib(), name)
+    raw = [a.data_ptr() if isinstance(a, torch.Tensor) else a for a in args]
+    raw.append(torch.cuda.current_stream().cuda_stream)
+
+    def call():
+        st = fn(*raw)
+        if st != 0:
+            raise RuntimeError(f"{name}: {F.fp8ds_status_string(st)}")
+    return call
+
+
 def _nsets(bytes_per_call):
     """Buffer sets for cold_rotating: the others' traffic exceeds ROTATE_BYTES, at least 3 sets."""
     return max(3, 1 + -(-ROTATE_BYTES // bytes_per_call))
@@ -374,7 +390,8 @@ def cast_family(F, S, torch, np, dev, bf16):
     """Cold timings of the cast family at the sweep and backward-prep workloads: cast+transpose
     of N(0,1) tensors with 0.1% outliers x1e3 at [1024,1024], [4096,4096], [8192,12288] (at the
     steady-state scale 0.4); cast+amax at [8192,12288]; dbias+cast+transpose of dy [8192,4096]
-    ~N(0,0.01) (E5M2, scale 4096) and the T=3, L=1024 scale update."""
+    ~N(0,0.01) (E5M2, scale 4096) and the T=3, L=1024 scale update.  Every call goes through the
+    C ABI with its arguments marshalled once (`_abi`)."""
     out = {}
     u8 = dict(device=dev, dtype=torch.uint8)
     f32 = dict(device=dev, dtype=torch.float32)
@@ -387,7 +404,7 @@ def cast_family(F, S, torch, np, dev, bf16):
         xs = [xd] + [xd.clone() for _ in range(ns - 1)]
         sets = [(x_, torch.empty((R, C), **u8), torch.empty((C, R), **u8)) for x_ in xs]
         sc, si, am = torch.tensor([0.4], **f32), torch.zeros(1, **f32), torch.zeros(1, **f32)
-        calls = [lambda x_=x_, o=o, ot=ot: F.fp8_cast_transpose(x_, sc, F.E4M3, o, ot, si, am) for x_, o, ot in sets]
+        calls = [_abi(F, torch, "fp8_cast_transpose", x_, R, C, sc, F.E4M3, o, ot, si, am, None) for x_, o, ot in sets]
         ms = cold_rotating(torch, calls, nbytes)
         gbps = nbytes / (ms * 1e-3) / 1e9
         sweep[f"{R}x{C}"] = {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
@@ -406,7 +423,8 @@ def cast_family(F, S, torch, np, dev, bf16):
     xs = [xd] + [xd.clone() for _ in range(_nsets(nbytes) - 1)]
     sets = [(x_, torch.empty((R * C,), **u8)) for x_ in xs]
     sc, si, am = torch.tensor([0.4], **f32), torch.zeros(1, **f32), torch.zeros(1, **f32)
-    ms = cold_rotating(torch, [lambda x_=x_, o=o: F.fp8_cast_amax(x_, sc, F.E4M3, o, si, am) for x_, o in sets], nbytes)
+    ms = cold_rotating(torch, [_abi(F, torch, "fp8_cast_amax", x_, R * C, sc, F.E4M3, o, si, am, None) for x_, o in sets],
+                       nbytes)
     out["cast_amax_8192x12288_cold"] = {"us": round(ms * 1e3, 2), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
                                         "frac_hbm": round(nbytes / (ms * 1e-3) / HBM_PEAK, 3)}
     del xs, sets, xd
@@ -419,14 +437,15 @@ def cast_family(F, S, torch, np, dev, bf16):
     sets = [(x_, torch.empty((R, C), **u8), torch.empty((C, R), **u8), torch.empty(C, **f32),
              torch.zeros(F.fp8_dbias_workspace_bytes(R, C), **u8)) for x_ in xs]
     sc, si, am = torch.tensor([4096.0], **f32), torch.zeros(1, **f32), torch.zeros(1, **f32)
-    ms = cold_rotating(torch, [lambda x_=x_, o=o, ot=ot, d=d, w=w: F.fp8_dbias_cast_transpose(x_, sc, F.E5M2, o, ot, d,
-                                                                                            w, si, am)
-                               for x_, o, ot, d, w in sets], nbytes)
+    ms = cold_rotating(torch, [_abi(F, torch, "fp8_dbias_cast_transpose", x_, R, C, sc, F.E5M2, o, ot, si, am, d, w,
+                                    w.numel()) for x_, o, ot, d, w in sets], nbytes)
     h = torch.from_numpy(S.log_uniform_f32(S.seed_for(3, 1), 1024 * 3, 1e-3, 1e3).reshape(1024, 3)).to(dev)
     s3, si3 = torch.ones(3, **f32), torch.ones(3, **f32)
     F.fp8_scale_update(h, s3, si3, [0, 0, 1], 0)
     torch.cuda.synchronize()
-    us_upd = _time_fn(torch, lambda: F.fp8_scale_update(h, s3, si3, [0, 0, 1], 0), 50) * 1e3
+    fmts = (ctypes.c_int32 * 3)(0, 0, 1)
+    us_upd = _time_fn(torch, _abi(F, torch, "fp8_scale_update", h, 1024, 3, s3, si3, ctypes.cast(fmts, ctypes.c_void_p), 0),
+                      50) * 1e3
     out["backward_prep"] = {"dbias_cast_transpose_8192x4096_us": round(ms * 1e3, 2),
                             "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
                             "frac_hbm": round(nbytes / (ms * 1e-3) / HBM_PEAK, 3),

@@ -178,11 +178,14 @@ __device__ __forceinline__ void ct_tile_of(uint32_t block, int64_t rows, uint32_
     }
 }
 
-template <int FMT, bool VEC, bool DBIAS>
-__global__ __launch_bounds__(kCtThreads) void k_cast_transpose(const CtBatch batch, float *__restrict__ partial) {
-    __shared__ __align__(16) uint8_t tT[kTileC * kTile];
+template <int FMT, bool VEC, bool DBIAS, int TS = kTile>
+__global__ __launch_bounds__((TS / 8) * (TS / 8)) void k_cast_transpose(const CtBatch batch, float *__restrict__ partial) {
+    // TS x TS tiles: 256 (1024 threads) in general, 64 (64 threads) for tensors of few tiles
+    constexpr int NRB = TS / 8, NT = NRB * NRB, CH = TS / 16;
+    static_assert(!DBIAS || TS == kTile, "the dbias partials are per 256-row tile");
+    __shared__ __align__(16) uint8_t tT[TS * TS];
     __shared__ float csum[DBIAS ? kRowBlocks * kTileC : 1];
-    __shared__ uint32_t red[kCtThreads / 64];
+    __shared__ uint32_t red[NT / 64];
     // Both tensors' fields are kernel arguments: selecting values (not a pointer to one tensor)
     // lets every argument load go out in one round, and the first input loads follow it.
     const bool second = (int64_t)blockIdx.x >= batch.first1;
@@ -199,18 +202,23 @@ __global__ __launch_bounds__(kCtThreads) void k_cast_transpose(const CtBatch bat
     const float skip_flag = noop != nullptr ? *noop : 0.0f;
 
     const int t = threadIdx.x;
-    const int rb = t >> 5, cb = t & 31;
+    const int rb = t / NRB, cb = t % NRB;
     const uint32_t block = blockIdx.x - (second ? (uint32_t)batch.first1 : 0u);
-    const uint32_t tiles_c = (uint32_t)((cols + kTileC - 1) / kTileC);
+    const uint32_t tiles_c = (uint32_t)((cols + TS - 1) / TS);
     uint32_t tile_r, tile_c;
-    ct_tile_of(block, rows, tiles_c, tile_r, tile_c);
-    const int64_t r0 = (int64_t)tile_r * kTile;
-    const int64_t c0 = (int64_t)tile_c * kTileC;
+    if (TS == kTile) {
+        ct_tile_of(block, rows, tiles_c, tile_r, tile_c);
+    } else {
+        tile_r = block / tiles_c;
+        tile_c = block - tile_r * tiles_c;
+    }
+    const int64_t r0 = (int64_t)tile_r * TS;
+    const int64_t c0 = (int64_t)tile_c * TS;
     const int64_t row = r0 + rb * 8;   // first row of the micro-tile
     const int64_t col = c0 + cb * 8;   // first column of the micro-tile
     // Interior tile (block-uniform): every access of the 16-byte path is in bounds, so loads and
     // stores go out unconditionally (per-access checks put each one in a branch of its own).
-    const bool full = VEC && r0 + kTile <= rows && c0 + kTileC <= cols;
+    const bool full = VEC && r0 + TS <= rows && c0 + TS <= cols;
 
     // ---- load 8 rows x 8 columns (bfloat16 pairs in dwords: w[r][0..3])
     uint32_t w[8][4];
@@ -340,7 +348,7 @@ __global__ __launch_bounds__(kCtThreads) void k_cast_transpose(const CtBatch bat
         for (int c = 0; c < 8; ++c) {
             const int tc = cb * 8 + c;
             u32x2 v = {ocol[c][0], ocol[c][1]};
-            *reinterpret_cast<u32x2 *>(&tT[tc * kTile + ((rb ^ t_swz(tc)) << 3)]) = v;
+            *reinterpret_cast<u32x2 *>(&tT[tc * TS + ((rb ^ ((tc >> 3) & (NRB - 1))) << 3)]) = v;
         }
     }
 
@@ -349,13 +357,13 @@ __global__ __launch_bounds__(kCtThreads) void k_cast_transpose(const CtBatch bat
     // ---- transposed tile out: 256 transposed rows x 256 bytes, 16-byte chunks
     if (want_t)
 #pragma unroll
-    for (int i = 0; i < (kTileC * kTile / 16) / kCtThreads; ++i) {
-        const int q = t + kCtThreads * i;
-        const int tr = q >> 4, part = q & 15;          // transposed row (= tile column), chunk
+    for (int i = 0; i < (TS * TS / 16) / NT; ++i) {
+        const int q = t + NT * i;
+        const int tr = q / CH, part = q % CH;          // transposed row (= tile column), chunk
         const int64_t orow_g = c0 + tr;                 // row of out_t
         const int64_t ocol_g = r0 + part * 16;          // first column of out_t in this chunk
-        const int g = t_swz(tr);
-        u32x4 v = *reinterpret_cast<const u32x4 *>(&tT[tr * kTile + ((part ^ (g >> 1)) << 4)]);
+        const int g = (tr >> 3) & (NRB - 1);
+        u32x4 v = *reinterpret_cast<const u32x4 *>(&tT[tr * TS + ((part ^ (g >> 1)) << 4)]);
         if (g & 1) v = v.zwxy;
         if (full) {
             __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(out_t + orow_g * rows + ocol_g));
@@ -383,7 +391,7 @@ __global__ __launch_bounds__(kCtThreads) void k_cast_transpose(const CtBatch bat
     }
 
     // ---- amax: one atomic per block; inverse scale from block (0, 0)
-    uint32_t bm = block_max_u32<kCtThreads>(mag, red);
+    uint32_t bm = block_max_u32<NT>(mag, red);
     if (t == 0) {
         fold_amax(amax_slot, bm);
         if (block == 0 && sinv_out != nullptr) *sinv_out = 1.0f / s;
@@ -655,20 +663,40 @@ hipError_t launch_cast_amax(const uint16_t *x, int64_t n, const float *scale, in
     return hipGetLastError();
 }
 
-static int64_t ct_tiles(int64_t rows, int64_t cols) {
-    return ((cols + kTileC - 1) / kTileC) * ((rows + kTile - 1) / kTile);
+static int64_t ct_tiles(int64_t rows, int64_t cols, int ts = kTile) {
+    return ((cols + ts - 1) / ts) * ((rows + ts - 1) / ts);
 }
 static bool ct_vec(int64_t rows, int64_t cols) { return (cols % 8 == 0) && (rows % 16 == 0); }
 
+// Launches that would have fewer 256 x 256 tiles than this take 64 x 64 tiles of 64 threads:
+// with few tiles the 1024-thread blocks leave most CUs idle and each tile is a long chain of
+// dependent steps.  Measured on the same buffers (E4M3, cold): [1024, 1024] 3.9 us against
+// 7.3 us, [2048, 2048] 5.1 against 7.8 us; at [4096, 4096] (256 tiles) the 256 x 256 tile is
+// faster, 13.3 against 18.4 us.
+constexpr int kSmallTs = 64;
+constexpr int64_t kSmallCastTiles = 128;
+
 template <bool DBIAS>
-static hipError_t launch_batch(const CtBatch &b, int64_t blocks, bool vec, int fmt, float *partial, hipStream_t st) {
+static hipError_t launch_batch(const CtBatch &b, int64_t blocks, bool vec, bool small, int fmt, float *partial,
+                               hipStream_t st) {
     dim3 grid((unsigned)blocks);
-#define FP8DS_CT(F, V) k_cast_transpose<F, V, DBIAS><<<grid, dim3(kCtThreads), 0, st>>>(b, partial)
-    if (fmt == kE4M3) {
-        if (vec) FP8DS_CT(kE4M3, true); else FP8DS_CT(kE4M3, false);
-    } else {
-        if (vec) FP8DS_CT(kE5M2, true); else FP8DS_CT(kE5M2, false);
+#define FP8DS_CT(F, V, TS_) k_cast_transpose<F, V, DBIAS, TS_><<<grid, dim3((TS_ / 8) * (TS_ / 8)), 0, st>>>(b, partial)
+#define FP8DS_CT_FMT(TS_)                                                                                  \
+    do {                                                                                                   \
+        if (fmt == kE4M3) {                                                                                \
+            if (vec) FP8DS_CT(kE4M3, true, TS_); else FP8DS_CT(kE4M3, false, TS_);                         \
+        } else {                                                                                           \
+            if (vec) FP8DS_CT(kE5M2, true, TS_); else FP8DS_CT(kE5M2, false, TS_);                         \
+        }                                                                                                  \
+    } while (0)
+    if constexpr (!DBIAS) {
+        if (small) {
+            FP8DS_CT_FMT(kSmallTs);
+            return hipGetLastError();
+        }
     }
+    FP8DS_CT_FMT(kTile);
+#undef FP8DS_CT_FMT
 #undef FP8DS_CT
     return hipGetLastError();
 }
@@ -680,9 +708,10 @@ static hipError_t launch_ct(const uint16_t *x, int64_t rows, int64_t cols, const
     CtBatch b{};
     b.t[0] = CtTensor{x, rows, cols, scale, out, out_t, sinv_out, amax_slot, noop};
     b.t[1] = b.t[0];
-    const int64_t n = ct_tiles(rows, cols);
+    const bool small = !DBIAS && ct_tiles(rows, cols) < kSmallCastTiles;
+    const int64_t n = ct_tiles(rows, cols, small ? kSmallTs : kTile);
     b.first1 = n;
-    return launch_batch<DBIAS>(b, n, ct_vec(rows, cols), fmt, partial, st);
+    return launch_batch<DBIAS>(b, n, ct_vec(rows, cols), small, fmt, partial, st);
 }
 
 hipError_t launch_cast_transpose(const uint16_t *x, int64_t rows, int64_t cols, const float *scale, int fmt,
@@ -698,21 +727,24 @@ hipError_t launch_cast_transpose_pair(const uint16_t *x0, int64_t rows0, int64_t
                                       uint8_t *out1, uint8_t *out_t1, float *sinv1, float *amax1, const float *noop1,
                                       int fmt, hipStream_t st) {
     const bool v0 = ct_vec(rows0, cols0), v1 = ct_vec(rows1, cols1);
-    const int64_t n0 = (rows0 == 0 || cols0 == 0) ? 0 : ct_tiles(rows0, cols0);
-    const int64_t n1 = (rows1 == 0 || cols1 == 0) ? 0 : ct_tiles(rows1, cols1);
-    if (v0 != v1 || n0 == 0 || n1 == 0) {
+    const bool e0 = rows0 == 0 || cols0 == 0, e1 = rows1 == 0 || cols1 == 0;
+    if (v0 != v1 || e0 || e1) {
         // the two tensors need different code paths (or one is empty): one launch each
         hipError_t e = hipSuccess;
-        if (n0) e = launch_ct<false>(x0, rows0, cols0, scale0, fmt, out0, out_t0, sinv0, amax0, noop0, nullptr, st);
-        if (e == hipSuccess && n1)
+        if (!e0) e = launch_ct<false>(x0, rows0, cols0, scale0, fmt, out0, out_t0, sinv0, amax0, noop0, nullptr, st);
+        if (e == hipSuccess && !e1)
             e = launch_ct<false>(x1, rows1, cols1, scale1, fmt, out1, out_t1, sinv1, amax1, noop1, nullptr, st);
         return e;
     }
+    // one tile size for both: the small one when the pair together has few tiles
+    const bool small = ct_tiles(rows0, cols0) + ct_tiles(rows1, cols1) < kSmallCastTiles;
+    const int ts = small ? kSmallTs : kTile;
+    const int64_t n0 = ct_tiles(rows0, cols0, ts), n1 = ct_tiles(rows1, cols1, ts);
     CtBatch b{};
     b.t[0] = CtTensor{x0, rows0, cols0, scale0, out0, out_t0, sinv0, amax0, noop0};
     b.t[1] = CtTensor{x1, rows1, cols1, scale1, out1, out_t1, sinv1, amax1, noop1};
     b.first1 = n0;
-    return launch_batch<false>(b, n0 + n1, v0, fmt, nullptr, st);
+    return launch_batch<false>(b, n0 + n1, v0, small, fmt, nullptr, st);
 }
 
 // Workspace: the strip counters of the one-launch form (kStripCounterBytes, zero between

@@ -73,7 +73,11 @@ def _run_ct(xh, scale, fmt, noop=None):
     return u8_host(out), u8_host(out_t), slot.item(), sinv.cpu().numpy()[0]
 
 
-CT_SHAPES = [(1, 1), (3, 5), (16, 8), (128, 128), (130, 264), (144, 264), (257, 383), (1040, 776), (1024, 1024)]
+# Below 128 tiles of 256 x 256 the launch takes 64 x 64 tiles ((2048, 3840): 120 tiles, the largest
+# here); (4112, 2056) and (3000, 3001) take ragged 256 x 256 tiles on the 16-byte path and on
+# the element-wise path.
+CT_SHAPES = [(1, 1), (3, 5), (16, 8), (128, 128), (130, 264), (144, 264), (257, 383), (1040, 776), (1024, 1024),
+             (2048, 3840), (4112, 2056), (3000, 3001)]
 
 
 @pytest.mark.parametrize("fmt", [F.E4M3, F.E5M2])
