@@ -76,6 +76,10 @@ def test_dbias_noalloc_rejects_sizes_beyond_its_scratch():
     f.restype = ctypes.c_int
     # 32 row blocks x 80000 columns x 4 bytes = 10.24 MB of partials > 8 MiB: rejected, nothing launched
     assert F.fp8_dbias_workspace_bytes(8192, 80000) > 8 << 20
+    # the limit: 1 KiB of strip counters + 32 x cols x 4 bytes <= 8 MiB, so 8192 rows fit up to 65528 columns
+    assert F.fp8_dbias_workspace_bytes(8192, 65528) == 8 << 20
+    assert F.fp8_dbias_workspace_bytes(8192, 65536) > 8 << 20
+    assert f(A16, 8192, 65536, A16, 1, A16, A16, None, None, A16, None) == -8
     assert f(A16, 8192, 80000, A16, 1, A16, A16, None, None, A16, None) == -8
     assert f(A16, -1, 100, A16, 1, A16, A16, None, None, A16, None) == -2
 
