@@ -48,7 +48,7 @@ def _equal(a, b):
     assert torch.equal(a.y.view(torch.int16), b.y.view(torch.int16))
 
 
-# C1 ([128, 256] x [256, 256]), a ragged M, a narrow N, a deep K, the largest tile count
+# the small layer [128, 256] x [256, 256], a ragged M, a narrow N, a deep K, the largest tile count
 @pytest.mark.parametrize("shape", [(128, 256, 256), (100, 48, 512), (64, 1024, 1024), (130, 16, 8192),
                                    (1536, 1536, 256)])
 @pytest.mark.parametrize("with_bias", [True, False])
