@@ -1,0 +1,106 @@
+"""Seeded random shapes through the size-dependent code paths: cast+transpose (64 x 64 tiles below
+128 tiles of 256 x 256, else 256 x 256; the 16-byte path and the element-wise path), dbias + cast
++ transpose (the one-launch strip form for tensors of whole tiles with at most two tiles per CU,
+else the tile kernel + reduction), and the forward of a layer (one launch for small layers,
+else the cast launch + GEMM).  Every code, transpose, amax and inverse scale against the oracle
+bit for bit; dbias and y within their bounds."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_delayed_scaling_amd as F
+import oracle
+import synthetic as S
+from helpers import DEV, bf16_dev, f32_bits, gemm_close, scalar, to_f64, u8_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw(seed, k, lo, hi):
+    """k seeded integers in [lo, hi]."""
+    return [lo + int(u * (hi - lo + 1)) for u in S.uniform(seed, 0, k)]
+
+
+def _ct_shapes():
+    rows = _draw(S.seed_for(10, 0), 8, 1, 6000) + _draw(S.seed_for(10, 14), 4, 3000, 9000)
+    cols = _draw(S.seed_for(10, 1), 8, 1, 6000) + _draw(S.seed_for(10, 15), 4, 3000, 9000)
+    # every other shape rounded to the 16-byte path's multiples
+    return [(r - r % 16 or 16, c - c % 8 or 8) if i % 2 else (r, c) for i, (r, c) in enumerate(zip(rows, cols))]
+
+
+@pytest.mark.parametrize("shape", _ct_shapes())
+def test_cast_transpose_random_shapes(shape):
+    R, C = shape
+    print(f"cast_transpose random shape {shape}", flush=True)
+    xh = S.outlier_bf16(S.seed_for(10, 2 + R % 7), shape, 1.0)
+    x = bf16_dev(xh)
+    out = torch.full((R, C), 0xAB, dtype=torch.uint8, device=DEV)
+    out_t = torch.full((C, R), 0xCD, dtype=torch.uint8, device=DEV)
+    sinv, slot = scalar(-1.0), scalar(0.0)
+    F.fp8_cast_transpose(x, scalar(3.0), F.E4M3, out, out_t, sinv, slot)
+    torch.cuda.synchronize()
+    rq, rqt, ra, rs = oracle.cast_transpose(xh, 3.0, F.E4M3)
+    assert np.array_equal(u8_host(out), rq) and np.array_equal(u8_host(out_t), rqt)
+    assert f32_bits(slot.item()) == f32_bits(ra) and f32_bits(sinv.item()) == f32_bits(rs)
+
+
+def _dbias_shapes():
+    # whole-tile shapes: tiles_r in [1, 32], tiles_c in [1, 40], some with at most 512 tiles and
+    # two tiles per CU (strip form), some beyond (tile kernel); plus ragged shapes
+    tr = _draw(S.seed_for(10, 3), 6, 1, 32)
+    tc = _draw(S.seed_for(10, 4), 6, 1, 40)
+    whole = [(256 * a, 256 * b) for a, b in zip(tr, tc)]
+    ragged = list(zip(_draw(S.seed_for(10, 5), 3, 1, 5000), _draw(S.seed_for(10, 6), 3, 1, 3000)))
+    return whole + ragged
+
+
+@pytest.mark.parametrize("shape", _dbias_shapes())
+def test_dbias_random_shapes(shape):
+    R, C = shape
+    print(f"dbias random shape {shape}", flush=True)
+    dyh = S.normal_bf16(S.seed_for(10, 7 + R % 5), shape, 0.01)
+    dy = bf16_dev(dyh)
+    out = torch.full((R, C), 0xAB, dtype=torch.uint8, device=DEV)
+    out_t = torch.full((C, R), 0xCD, dtype=torch.uint8, device=DEV)
+    db = torch.full((C,), float("nan"), dtype=torch.float32, device=DEV)
+    ws = torch.zeros(F.fp8_dbias_workspace_bytes(R, C), dtype=torch.uint8, device=DEV)
+    sinv, slot = scalar(-1.0), scalar(0.0)
+    for rep in range(2):                      # the second call reuses the workspace as left
+        F.fp8_dbias_cast_transpose(dy, scalar(2048.0), F.E5M2, out, out_t, db, ws, sinv, slot)
+        torch.cuda.synchronize()
+        rq, rqt, ra, rs, rdb = oracle.dbias_cast_transpose(dyh, 2048.0, F.E5M2)
+        assert np.array_equal(u8_host(out), rq) and np.array_equal(u8_host(out_t), rqt), rep
+        assert f32_bits(slot.item()) == f32_bits(ra) and f32_bits(sinv.item()) == f32_bits(rs), rep
+        bound = 1e-5 * np.abs(S.bf16_bits_to_f64(dyh)).sum(axis=0) + 1e-30
+        assert np.all(np.abs(db.cpu().numpy().astype(np.float64) - rdb) <= bound), rep
+        assert not torch.any(ws[:1024]), rep
+
+
+def _fwd_shapes():
+    ms = _draw(S.seed_for(10, 8), 6, 1, 3000)
+    ns = [16 * n for n in _draw(S.seed_for(10, 9), 6, 1, 80)]
+    ks = [256 * k for k in _draw(S.seed_for(10, 10), 6, 1, 8)]
+    return list(zip(ms, ns, ks))
+
+
+@pytest.mark.parametrize("shape", _fwd_shapes())
+def test_linear_fwd_random_shapes(shape):
+    M, N, K = shape
+    print(f"linear fwd random shape {shape}", flush=True)
+    xh = S.normal_bf16(S.seed_for(10, 11), (M, K), 1.0)
+    wh = S.normal_bf16(S.seed_for(10, 12), (N, K), 0.5)
+    bh = S.normal_bf16(S.seed_for(10, 13), (N,), 0.1)
+    u8 = dict(dtype=torch.uint8, device=DEV)
+    x8, w8, w8t = torch.empty((M, K), **u8), torch.empty((N, K), **u8), torch.empty((K, N), **u8)
+    am, si = torch.zeros(2, device=DEV), torch.zeros(2, device=DEV)
+    sc = torch.tensor([2.0, 30.0], device=DEV)
+    y = torch.empty((M, N), device=DEV, dtype=torch.bfloat16)
+    F.fp8_linear_fwd(bf16_dev(xh), bf16_dev(wh), bf16_dev(bh), sc[0:1], am[0:1], x8, None, si[0:1], sc[1:2], am[1:2],
+                     w8, w8t, si[1:2], None, y)
+    torch.cuda.synchronize()
+    fw = oracle.linear_fwd(xh, wh, bh, 2.0, 30.0, want_x_t=False)
+    assert np.array_equal(u8_host(x8), fw["x8"])
+    assert np.array_equal(u8_host(w8), fw["w8"]) and np.array_equal(u8_host(w8t), fw["w8t"])
+    assert np.array_equal(f32_bits(am.cpu().numpy()), f32_bits(np.array([fw["x_amax"], fw["w_amax"]], np.float32)))
+    assert np.array_equal(f32_bits(si.cpu().numpy()), f32_bits(np.array([fw["x_sinv"], fw["w_sinv"]], np.float32)))
+    gemm_close(to_f64(y), fw["y"], bf16_out=True)
