@@ -7,10 +7,12 @@
 //
 // All three are HBM-streaming kernels.  Reads are 16-byte per lane and coalesced along rows;
 // the FP8 codes are produced by the hardware converter after a v_med3 clamp (saturation);
-// the transposed copy is built by converting column pairs straight into packed dwords and
-// exchanging 8-byte fragments through LDS, so both outputs leave in coalesced stores.
-// The amax is a packed 16-bit integer max of the bfloat16 magnitudes, reduced per wave and
-// per block, with one atomic per block.
+// each row's codes are converted once, and the transposed copy is made from them by 4 x 4 byte
+// transposes in registers (v_perm_b32) staged through an LDS tile, so both outputs leave in
+// coalesced stores.  dbias + cast + transpose has two forms: the tile kernel writing per-tile
+// column sums plus a reduction launch, and a one-launch strip form for tensors of few whole
+// tiles.  The amax is a packed 16-bit integer max of the bfloat16 magnitudes, reduced per wave
+// and per block, with one atomic per block.
 #include <algorithm>
 
 #include "../../include/fp8ds.h"

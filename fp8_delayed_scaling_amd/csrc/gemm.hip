@@ -25,8 +25,9 @@
 // the 8 XCDs) works on a contiguous range of tiles, walked in groups of kGroupM tile-rows for L2
 // reuse.  Epilogue: acc * a_scale_inv * b_scale_inv + bias in float32, rounded to bfloat16
 // (nearest even), stored as float32, or encoded to FP8 with amax capture (the pipelined kernels
-// stage it through LDS and write 16-byte row segments).  Ragged M / N are handled by clamping the
-// rows that are loaded and masking the stores.
+// stage bfloat16 and FP8 outputs through LDS and write 16-byte row segments; interior float32
+// sub-tiles go straight from the accumulators as whole 128-byte lines).  Ragged M / N are
+// handled by clamping the rows that are loaded and masking the stores.
 //
 // k_gemm_bias_pipe: a 4-stage pipeline of 64-byte K slices (4 x 32 KB of LDS).  Global memory goes
 // straight into LDS with buffer_load_dwordx4 ... lds (no staging registers; per-tile descriptors,
