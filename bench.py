@@ -603,6 +603,23 @@ def extras(F, S, torch, np, dev, bf16, step):
                                              "bf16_out_tflops": round(flop / (tb * 1e-3) / 1e12, 1)}
     del D8, Db
 
+    # the forward GEMM's speed against its operand bits: the step's own FP8 operands, then the
+    # same shapes of zero codes (identical instructions; only the bits the matrix units and data
+    # paths toggle differ, and with them the power drawn and the clock the chip holds)
+    xz, wz = torch.zeros_like(step["x8"]), torch.zeros_like(step["w8"])
+    Mf, Kf = step["x8"].shape
+    Nf = step["w8"].shape[0]
+    Df = torch.empty((Mf, Nf), device=dev, dtype=torch.bfloat16)
+    sx, sw = step["sinv"][0:1], step["sinv"][1:2]
+    flop = 2.0 * Mf * Nf * Kf
+    tr = tz = float("inf")
+    for _ in range(3):
+        tr = min(tr, _time_fn(torch, lambda: F.fp8_gemm_bias(step["x8"], F.E4M3, sx, step["w8"], F.E4M3, sw, None, Df), 5))
+        tz = min(tz, _time_fn(torch, lambda: F.fp8_gemm_bias(xz, F.E4M3, sx, wz, F.E4M3, sw, None, Df), 5))
+    out["gemm_fwd_operand_bits"] = {"step_operands_tflops": round(flop / (tr * 1e-3) / 1e12, 1),
+                                    "zero_operands_tflops": round(flop / (tz * 1e-3) / 1e12, 1)}
+    del xz, wz, Df
+
     del flush
     torch.cuda.empty_cache()
     return out
