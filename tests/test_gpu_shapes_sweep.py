@@ -2,8 +2,9 @@
 128 tiles of 256 x 256, else 256 x 256; the 16-byte path and the element-wise path), dbias + cast
 + transpose (the one-launch strip form for tensors of whole tiles with at most two tiles per CU,
 else the tile kernel + reduction), and the forward of a layer (one launch for small layers,
-else the cast launch + GEMM).  Every code, transpose, amax and inverse scale against the oracle
-bit for bit; dbias and y within their bounds."""
+else the cast launch + GEMM), and the GEMM (both MFMA families, small-problem and 256 x 256
+kernels, all format pairs, bfloat16 and float32 output).  Every code, transpose, amax and
+inverse scale against the oracle bit for bit; dbias, y and D within their bounds."""
 import numpy as np
 import pytest
 import torch
@@ -104,3 +105,35 @@ def test_linear_fwd_random_shapes(shape):
     assert np.array_equal(f32_bits(am.cpu().numpy()), f32_bits(np.array([fw["x_amax"], fw["w_amax"]], np.float32)))
     assert np.array_equal(f32_bits(si.cpu().numpy()), f32_bits(np.array([fw["x_sinv"], fw["w_sinv"]], np.float32)))
     gemm_close(to_f64(y), fw["y"], bf16_out=True)
+
+
+def _gemm_cases():
+    ms = _draw(S.seed_for(10, 16), 10, 1, 3000)
+    ns = _draw(S.seed_for(10, 17), 10, 1, 3000)
+    # K: five multiples of 16 (the 32 x 32 x 64 family unless K % 256 == 0), five of 256
+    ks = [16 * k for k in _draw(S.seed_for(10, 18), 5, 1, 160)] + [256 * k for k in _draw(S.seed_for(10, 19), 5, 1, 10)]
+    pairs = _draw(S.seed_for(10, 20), 10, 0, 3)   # (A format, B format) = (p >> 1, p & 1)
+    outs = _draw(S.seed_for(10, 21), 10, 0, 1)    # bfloat16 or float32 output
+    return list(zip(ms, ns, ks, pairs, outs))
+
+
+@pytest.mark.parametrize("case", _gemm_cases())
+def test_gemm_random_shapes(case):
+    """Seeded random GEMM shapes, format pairs and output dtypes (small-problem and 256 x 256
+    kernels of both MFMA families, ragged M, N and K): full sampled rows and columns against the
+    float64 oracle."""
+    M, N, K, p, od = case
+    fa, fb = p >> 1, p & 1
+    print(f"gemm random M={M} N={N} K={K} fa={fa} fb={fb} out={od}", flush=True)
+    A8 = oracle.cast_amax(S.normal_bf16(S.seed_for(10, 22), (M, K), 2.0), 1.0, fa)[0]
+    B8 = oracle.cast_amax(S.normal_bf16(S.seed_for(10, 23), (N, K), 2.0), 1.0, fb)[0]
+    bias = S.normal_bf16(S.seed_for(10, 24), (N,), 0.1)
+    D = torch.full((M, N), float("nan"), device=DEV, dtype=torch.bfloat16 if od == 0 else torch.float32)
+    F.fp8_gemm_bias(torch.from_numpy(A8).to(DEV), fa, scalar(0.5), torch.from_numpy(B8).to(DEV), fb, scalar(0.25),
+                    bf16_dev(bias), D)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, M - 1], (S.uniform(S.seed_for(10, 25), 0, 30) * M).astype(np.int64)]))
+    cols = np.unique(np.concatenate([[0, N - 1], (S.uniform(S.seed_for(10, 26), 0, 30) * N).astype(np.int64)]))
+    R_rows, R_cols = oracle.gemm_bias_sampled(A8, fa, 0.5, B8, fb, 0.25, bias, rows, cols)
+    gemm_close(to_f64(D[torch.from_numpy(rows).to(DEV)]), R_rows, bf16_out=(od == 0))
+    gemm_close(to_f64(D[:, torch.from_numpy(cols).to(DEV)]), R_cols, bf16_out=(od == 0))
