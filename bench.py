@@ -521,8 +521,26 @@ def extras(F, S, torch, np, dev, bf16, step):
         L.fp8_linear_fwd(*raw_args)
     torch.cuda.synchronize()
     raw_us = (time.perf_counter() - t) / 200 * 1e6
+    # the captured graph launched with hipGraphLaunch itself (what a C caller replaying it pays,
+    # without torch's replay bookkeeping); the HIP runtime is the one torch already loaded
+    hip_graph_us = None
+    try:
+        hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+        hip.hipGraphLaunch.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipGraphLaunch.restype = ctypes.c_int
+        gexec, gst = int(g.raw_cuda_graph_exec()), torch.cuda.current_stream().cuda_stream
+        if hip.hipGraphLaunch(gexec, gst) == 0:
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            for _ in range(200):
+                hip.hipGraphLaunch(gexec, gst)
+            torch.cuda.synchronize()
+            hip_graph_us = round((time.perf_counter() - t) / 200 * 1e6, 2)
+    except (OSError, AttributeError, TypeError, ValueError, RuntimeError):
+        pass
     out["small_forward_128x256x256"] = {"eager_us_per_call": round(eager_us, 2), "graph_replay_us": round(graph_us, 2),
-                                        "c_abi_eager_us_per_call": round(raw_us, 2), "launches": 1}
+                                        "c_abi_eager_us_per_call": round(raw_us, 2),
+                                        "hip_graph_launch_us": hip_graph_us, "launches": 1}
 
     # N-chunked GEMM + bias, M=8192, K=N=12288 (x8 and the first 12288 rows of W8), one stream
     # per chunk, captured as one graph
