@@ -1497,11 +1497,17 @@ hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64
     return hipGetLastError();
 }
 
-// The one-launch small forward applies when the GEMM takes the small 16 x 16 x 128 kernel
-// (K % 256 == 0, fewer than kSmallTiles tiles of 256 x 256), K <= 8192, N % 16 == 0 (whole
-// 16-byte chunks of w8_t rows) and x's transpose is not asked for.
+// The one-launch small forward applies where it beats the cast-pair launch + GEMM launch: K ==
+// 256 (two 128-byte steps; each further step adds a memory round trip that the one-launch
+// kernel does not hide: measured through the C ABI, 10.8 against 9.6 us at [128, 256, 512],
+// 35 against 16 us at K = 2048), at most 256 blocks of 64 x 64 (one per CU: 7.7 against 8.5 us
+// at [1024, 1024, 256], 10.2 against 9.6 us at [768, 1536, 256]), fewer than kSmallTiles tiles of
+// 256 x 256 (the GEMM of the two-launch form is then k_gemm_small16, whose bits it reproduces),
+// N % 16 == 0 (whole 16-byte chunks of w8_t rows), and x's transpose not asked for.
+constexpr int64_t kSmallFwdMaxBlocks = 256;
 bool linear_fwd_small_ok(int64_t M, int64_t N, int64_t K, const uint8_t *x8_t) {
-    if (x8_t != nullptr || M <= 0 || N <= 0 || K <= 0 || K % kFam16K != 0 || K > 8192 || N % 16 != 0) return false;
+    if (x8_t != nullptr || M <= 0 || N <= 0 || K != kFam16K || N % 16 != 0) return false;
+    if (((M + kSmallTile - 1) / kSmallTile) * ((N + kSmallTile - 1) / kSmallTile) > kSmallFwdMaxBlocks) return false;
     return ((M + BM - 1) / BM) * ((N + BN - 1) / BN) < kSmallTiles;
 }
 

@@ -1,8 +1,9 @@
-"""The one-launch forward of small layers (fp8_linear_fwd when K % 256 == 0, K <= 8192, N % 16
-== 0, no x transpose and fewer than 40 output tiles of 256 x 256) against the individual calls
-(cast of x, cast+transpose of W, GEMM + bias: every output bit for bit) and against the oracle
-(codes, amaxes and inverse scales exact, y within the GEMM tolerance), including the cached-
-weight flag, non-finite inputs, scales that are not plain, and graph replay."""
+"""The one-launch forward of small layers (fp8_linear_fwd when K == 256, N % 16 == 0, no x
+transpose, at most 256 output blocks of 64 x 64 and fewer than 40 of 256 x 256) against the
+individual calls (cast of x, cast+transpose of W, GEMM + bias: every output bit for bit) and
+against the oracle (codes, amaxes and inverse scales exact, y within the GEMM tolerance),
+including the cached-weight flag, non-finite inputs, scales that are not plain, graph replay, and
+the layers just outside the rule (which take the cast launch + GEMM launch)."""
 import numpy as np
 import pytest
 import torch
@@ -48,9 +49,10 @@ def _equal(a, b):
     assert torch.equal(a.y.view(torch.int16), b.y.view(torch.int16))
 
 
-# the small layer [128, 256] x [256, 256], a ragged M, a narrow N, a deep K, the largest tile count
-@pytest.mark.parametrize("shape", [(128, 256, 256), (100, 48, 512), (64, 1024, 1024), (130, 16, 8192),
-                                   (1536, 1536, 256)])
+# the small layer [128, 256] x [256, 256], a ragged M, a narrow N, a wide N, the largest block
+# count (16 x 16 blocks of 64 x 64); then layers outside the rule: K = 512 and 8192, 288 blocks
+@pytest.mark.parametrize("shape", [(128, 256, 256), (100, 48, 256), (64, 1024, 256), (130, 16, 256), (1024, 1024, 256),
+                                   (100, 48, 512), (130, 16, 8192), (768, 1536, 256)])
 @pytest.mark.parametrize("with_bias", [True, False])
 def test_one_launch_equals_primitives_and_oracle(shape, with_bias):
     M, N, K = shape
@@ -106,7 +108,7 @@ def test_one_launch_cached_weight_and_graph():
     """With the weight's flag at 1 the layer multiplies by the cached codes and inverse scale and
     writes nothing of W (a changed bfloat16 W is not seen); captured once and replayed with the
     flag and x changing between replays, every replay equals the individual calls."""
-    M, N, K = 128, 256, 512
+    M, N, K = 128, 256, 256
     xh = [S.normal_bf16(S.seed_for(9, 10 + k), (M, K), 1.0) for k in range(3)]
     wh0 = S.normal_bf16(S.seed_for(9, 20), (N, K), 1.0)
     wh1 = S.normal_bf16(S.seed_for(9, 21), (N, K), 3.0)
@@ -144,3 +146,36 @@ def test_one_launch_cached_weight_and_graph():
         fw = oracle.linear_fwd(xh[k], wh0, bh, 4.0, 16.0, want_x_t=False)
         assert np.array_equal(u8_host(a.w8), fw["w8"]) and np.array_equal(u8_host(a.w8t), fw["w8t"])
         gemm_close(to_f64(a.y), fw["y"], bf16_out=True)
+
+
+def _kernel_names(fn):
+    """Names of the GPU kernels ``fn`` launches (torch's profiler), or None when it records none."""
+    from torch.profiler import ProfilerActivity, profile
+    torch.cuda.synchronize()
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        fn()
+        torch.cuda.synchronize()
+    names = [e.name for e in prof.events() if e.device_type == torch.autograd.DeviceType.CUDA]
+    return names or None
+
+
+@pytest.mark.parametrize("shape, one", [((128, 256, 256), True), ((1024, 1024, 256), True), ((128, 256, 512), False),
+                                        ((768, 1536, 256), False)])
+def test_dispatch_rule_launches(shape, one):
+    """Inside the rule the forward is the single k_linear_fwd_small launch; outside it the cast
+    launch and the GEMM launch (both give the same bits; this checks which one ran)."""
+    M, N, K = shape
+    x = bf16_dev(S.normal_bf16(S.seed_for(9, 30), (M, K), 1.0))
+    w = bf16_dev(S.normal_bf16(S.seed_for(9, 31), (N, K), 1.0))
+    scales = torch.tensor([2.0, 48.0], **F32)
+    o = Fwd(M, N, K)
+    _layer_call(x, w, None, scales, o)
+    names = _kernel_names(lambda: _layer_call(x, w, None, scales, o))
+    if names is None:
+        pytest.skip("the profiler recorded no GPU kernels on this build")
+    fp8 = [n for n in names if "fp8ds" in n]
+    print(f"dispatch {shape}: {fp8}", flush=True)
+    if one:
+        assert len(fp8) == 1 and "k_linear_fwd_small" in fp8[0]
+    else:
+        assert not any("k_linear_fwd_small" in n for n in fp8) and len(fp8) == 2
