@@ -12,7 +12,7 @@
 //   * the 16 x 16 x 128 family (K % 256 == 0, row strides below 8 MiB; the hot path):
 //     k_gemm_pipe16 (256 x 256 tiles, 2 x 2 waves of 128 x 128 made of 8 x 8
 //     v_mfma_f32_16x16x128_f8f6f4 tiles) and k_gemm_small16 (one wave per 64 x 64 tile, for
-//     problems under 40 large tiles);
+//     problems of few large tiles: up to 32, 48 with K <= 1024, 64 with K == 256);
 //   * the 32 x 32 x 64 family (every other K % 16 == 0): k_gemm_bias_pipe (K % 64 == 0, strides
 //     below 8 MiB), k_gemm_small (K % 64 == 0, under 40 large tiles) and k_gemm_bias (general
 //     K, tail zero-filled), waves of 4 x 4 v_mfma_f32_32x32x64_f8f6f4 tiles.
@@ -939,10 +939,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pipe16(const uint8_t *__re
 // every element.
 // ------------------------------------------------------------------------------------------
 constexpr int kSmallTile = 64;
-// Below this many 256 x 256 tiles the small kernel is used: measured crossover on MI355X
-// (M x N x K = 1024 x 2048 x 4096, 32 tiles: small 38 us vs 44 us; 2048 x 2048 x 4096, 64 tiles:
-// small 72 us vs 44 us).
+// The 32 x 32 x 64 family takes its small kernel below this many 256 x 256 tiles (measured
+// crossover on MI355X: 1024 x 2048 x 4096, 32 tiles: small 38 us vs 44 us; 2048 x 2048 x 4096,
+// 64 tiles: small 72 us vs 44 us).
 constexpr int kSmallTiles = 40;
+// The 16 x 16 x 128 family's choice also weighs K: k_gemm_small16 keeps one wave per 64 x 64
+// tile, so it wins while its waves are few or short.  Kernel time per launch (graph of 20
+// launches, MI355X), small16 against pipe16: 25-32 tiles 33 vs 40 us at K = 4096; 36-48 tiles
+// 16.0-16.4 vs 17.5-17.8 us at K = 1024 but 27.7 vs 24.4 us at K = 2048; 64 tiles 8.7 vs
+// 12.7 us at K = 256 but 15.3 vs 14.8 us at K = 512; 80 tiles 12.5 vs 12.9 us at K = 256.
+__host__ __device__ constexpr bool small16_preferred(int64_t tiles, int64_t K) {
+    return tiles <= 32 || (tiles <= 48 && K <= 1024) || (tiles <= 64 && K <= 256);
+}
 
 template <int FA, int FB, int OUT>
 __global__ __launch_bounds__(64) void k_gemm_small(const uint8_t *__restrict__ A, int64_t lda,
@@ -1456,6 +1464,7 @@ hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64
     // the 16 x 16 x 128 family (k_gemm_pipe16 / k_gemm_small16, identical bits) for K % 256 == 0;
     // the choice depends on K and the strides only, so every N-chunk of a GEMM takes the same one
     const bool fam16 = (K % kFam16K) == 0 && pipe;
+    const bool small16 = fam16 && small16_preferred((int64_t)tiles_m * tiles_n, K);
     const int stiles_n = (int)((N + kSmallTile - 1) / kSmallTile);
     // bands of 8 tile-rows when the operands exceed the 256 MB Infinity Cache (block_tile)
     constexpr int64_t kInfinityCache = INT64_C(256) << 20;
@@ -1463,7 +1472,7 @@ hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64
     dim3 sgrid((unsigned)(((M + kSmallTile - 1) / kSmallTile) * stiles_n));
 #define FP8DS_GEMM(FA_, FB_, O_)                                                                           \
     do {                                                                                                   \
-        if (fam16 && small)                                                                                \
+        if (fam16 && small16)                                                                              \
             k_gemm_small16<FA_, FB_, O_><<<sgrid, dim3(64), 0, st>>>(                                      \
                 A, lda, B, ldb, a_sinv, b_sinv, bias, D, ldd, (int)M, (int)N, (int)K, stiles_n, oq);       \
         else if (fam16)                                                                                    \

@@ -232,8 +232,8 @@ def test_chunked_from_several_host_threads():
 @pytest.mark.parametrize("out_dtype", [0, 1])
 @pytest.mark.parametrize("shape", [(256, 16384, 512), (300, 16384, 320), (2048, 2048, 1024)])
 def test_small_problem_kernel_matches_large_tile_kernel(shape, out_dtype):
-    """Below 40 tiles of 256 x 256 the GEMM runs a one-wave 64 x 64 tile kernel.  These outputs
-    have 64 or more large tiles (large-tile kernel); each of their 8 N-chunks has 8 or 16 (small
+    """A GEMM of few 256 x 256 tiles runs a one-wave 64 x 64 tile kernel.  These outputs have 64
+    or more large tiles (large-tile kernel at their K); each of their 8 N-chunks has 8 or 16 (small
     kernel).  The MFMA sequence per element is the same, so the chunked output must equal the
     unchunked one bit for bit, ragged rows included."""
     M, N, K = shape
@@ -279,14 +279,15 @@ def test_gemm_pipelined_path_shapes(shape, fa, fb):
         assert torch.equal(D.view(torch.int32), Dg.view(torch.int32))
 
 
-@pytest.mark.parametrize("shape", [(1100, 2300, 256), (1500, 1800, 512), (2304, 1041, 1280), (4097, 700, 768),
-                                   (100, 12800, 256)])
+@pytest.mark.parametrize("shape", [(1100, 4100, 256), (1500, 2600, 512), (2304, 1041, 1280), (4097, 700, 768),
+                                   (100, 17000, 256)])
 @pytest.mark.parametrize("fa,fb", [(0, 0), (0, 1), (1, 0), (1, 1)])
 def test_gemm_fam16_large_tile_kernel(shape, fa, fb):
-    """K % 256 == 0 with 40 or more 256 x 256 tiles runs the 16 x 16 x 128 pipelined kernel: 2 to
-    10 K steps of 128 bytes, ragged M and N (partial tiles at both edges), every format pair,
+    """K % 256 == 0 with more 256 x 256 tiles than the small-problem kernel takes at that K (over
+    64 at K = 256, over 48 at K <= 1024, over 32 beyond) runs the 16 x 16 x 128 pipelined kernel:
+    2 to 10 K steps of 128 bytes, ragged M and N (partial tiles at both edges), every format pair,
     float32 and bfloat16 output against the oracle on sampled rows (the ragged last rows
-    included); the same GEMM cut into four N-chunks (under 40 tiles each) runs the small-problem
+    included); the same GEMM cut into four N-chunks (few tiles each) runs the small-problem
     kernel of the same family and must give the same bits."""
     M, N, K = shape
     print(f"gemm fam16 fa={fa} fb={fb} M={M} N={N} K={K}", flush=True)
