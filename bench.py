@@ -17,7 +17,8 @@ Also reported (own timings, HIP events on the launch stream):
   * dbias+cast+transpose of dy [8192, 4096] and the T=3, L=1024 scale update;
   * the forward-only small layer ([128,256] x [256,256]): eager and graph-replay latency;
   * N-chunked GEMM+bias M=8192, K=N=12288 in 4 and 8 chunks on their own streams, as a graph;
-  * the lazy transpose-cache fill of the FP8 weight [18432, 12288], cold (GB/s);
+  * the lazy transpose-cache fill of FP8 codes at the weight [18432, 12288] and activation
+    [8192, 12288] shapes, cold (GB/s);
   * the FP8-output GEMM (E5M2 output, own scale, amax capture) at the dgrad shape, against the
     bfloat16-output GEMM on the same operands;
   * a plain 1 GiB device copy, cold: the box's own streaming ceiling for the cast kernels;
@@ -586,16 +587,17 @@ def extras(F, S, torch, np, dev, bf16, step):
     out["copy_1GiB_cold"] = {"us": round(ms * 1e3, 1), "GBps": round(gbps, 1), "frac_hbm": round(gbps * 1e9 / HBM_PEAK, 3)}
     del src, dst
 
-    # lazy transpose-cache fill of the FP8 weight [18432, 12288], cold (1 B read + 1 B written)
-    Rw, Cw = 18432, 12288
-    W8 = torch.randint(0, 256, (Rw, Cw), generator=torch.Generator().manual_seed(9), dtype=torch.uint8).to(dev)
-    nbytes = Rw * Cw * 2
-    sets = [(W8 if k == 0 else W8.clone(), torch.empty((Cw, Rw), **u8)) for k in range(_nsets(nbytes))]
-    ms = cold_rotating(torch, [lambda a=a, b=b: F.fp8_transpose(a, b) for a, b in sets], nbytes)
-    gbps = nbytes / (ms * 1e-3) / 1e9
-    out["fp8_transpose_18432x12288_cold"] = {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
-                                              "frac_hbm": round(gbps * 1e9 / HBM_PEAK, 3)}
-    del W8, sets
+    # lazy transpose-cache fill of FP8 codes, cold (1 B read + 1 B written): the weight
+    # [18432, 12288] and the activation [8192, 12288] (seeded random bytes)
+    for Rw, Cw in ((18432, 12288), (8192, 12288)):
+        W8 = torch.randint(0, 256, (Rw, Cw), generator=torch.Generator().manual_seed(9), dtype=torch.uint8).to(dev)
+        nbytes = Rw * Cw * 2
+        sets = [(W8 if k == 0 else W8.clone(), torch.empty((Cw, Rw), **u8)) for k in range(_nsets(nbytes))]
+        ms = cold_rotating(torch, [lambda a=a, b=b: F.fp8_transpose(a, b) for a, b in sets], nbytes)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[f"fp8_transpose_{Rw}x{Cw}_cold"] = {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
+                                                 "frac_hbm": round(gbps * 1e9 / HBM_PEAK, 3)}
+        del W8, sets
 
     # GEMM writing an FP8 output with its own scale and amax capture, dgrad shape of the step
     # (M=8192, N=12288, K=18432), against the bfloat16-output GEMM on the same operands

@@ -27,18 +27,19 @@ def _run(xh, noop=None, prefill=0x5A):
     return u8_host(out)
 
 
-@pytest.mark.parametrize("shape", [(16, 16), (256, 256), (272, 528), (512, 4096), (4112, 48),
-                                   (1, 1), (17, 33), (300, 257), (1, 4000), (5000, 1), (255, 16)])
+# (512, 4096), (1024, 256) and (2048, 768) are whole 512 x 256 tiles (the 512-row kernel)
+@pytest.mark.parametrize("shape", [(16, 16), (256, 256), (272, 528), (512, 4096), (4112, 48), (1024, 256), (2048, 768),
+                                   (1, 1), (17, 33), (300, 257), (1, 4000), (5000, 1), (255, 16), (768, 256)])
 def test_transpose_parity(shape):
     print(f"fp8_transpose {shape}", flush=True)
     xh = _bytes(S.seed_for(30, shape[0] % 16), shape)
     assert np.array_equal(_run(xh), oracle.fp8_transpose(xh))
 
 
-@pytest.mark.parametrize("shape", [(18432, 12288), (8192, 18432)])
+@pytest.mark.parametrize("shape", [(18432, 12288), (8192, 18432), (8192, 12288)])
 def test_transpose_full_size(shape):
-    """The weight of the QKV projection at one TP=2 rank's share and its dy: the shapes whose
-    transpose cache the backward needs."""
+    """The weight of the QKV projection at one TP=2 rank's share, its dy and its x: the shapes
+    whose transpose cache the backward needs."""
     print(f"fp8_transpose full {shape}", flush=True)
     xh = _bytes(S.seed_for(31, 0), shape)
     assert np.array_equal(_run(xh), oracle.fp8_transpose(xh))
@@ -64,9 +65,11 @@ def test_transpose_empty_is_a_no_op():
     torch.cuda.synchronize()
 
 
-def test_transpose_noop_flag():
-    xh = _bytes(S.seed_for(33, 0), (272, 528))
-    stale = np.full((528, 272), 0x5A, np.uint8)
+@pytest.mark.parametrize("shape", [(272, 528), (512, 256)])
+def test_transpose_noop_flag(shape):
+    R, C = shape
+    xh = _bytes(S.seed_for(33, 0), (R, C))
+    stale = np.full((C, R), 0x5A, np.uint8)
     assert np.array_equal(_run(xh, noop=scalar(1.0)), oracle.fp8_transpose(xh, noop=True, out_t_prev=stale))
     assert np.array_equal(_run(xh, noop=scalar(0.0)), oracle.fp8_transpose(xh))
     assert np.array_equal(_run(xh, noop=scalar(0.5)), oracle.fp8_transpose(xh))   # only exactly 1.0 skips
