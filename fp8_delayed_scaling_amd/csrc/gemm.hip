@@ -14,7 +14,7 @@
 //     v_mfma_f32_16x16x128_f8f6f4 tiles) and k_gemm_small16 (one wave per 64 x 64 tile, for
 //     problems of few large tiles: up to 32, 48 with K <= 1024, 64 with K == 256);
 //   * the 32 x 32 x 64 family (every other K % 16 == 0): k_gemm_bias_pipe (K % 64 == 0, strides
-//     below 8 MiB), k_gemm_small (K % 64 == 0, under 40 large tiles) and k_gemm_bias (general
+//     below 8 MiB), k_gemm_small (K % 64 == 0, under 45 large tiles) and k_gemm_bias (general
 //     K, tail zero-filled), waves of 4 x 4 v_mfma_f32_32x32x64_f8f6f4 tiles.
 // Inside a family every output element is one fixed sequence of MFMAs over K in the same K
 // order, whatever kernel or tile it falls in, so the kernels of a family give identical bits
@@ -939,10 +939,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pipe16(const uint8_t *__re
 // every element.
 // ------------------------------------------------------------------------------------------
 constexpr int kSmallTile = 64;
-// The 32 x 32 x 64 family takes its small kernel below this many 256 x 256 tiles (measured
-// crossover on MI355X: 1024 x 2048 x 4096, 32 tiles: small 38 us vs 44 us; 2048 x 2048 x 4096,
-// 64 tiles: small 72 us vs 44 us).
-constexpr int kSmallTiles = 40;
+// The 32 x 32 x 64 family takes its small kernel below this many 256 x 256 tiles (kernel time
+// per launch on MI355X, small against pipelined: 36 tiles 24.5 vs 25.9 us at K = 2112, 40 tiles
+// 15.9 vs 19.1 us at K = 1088, 48 tiles 15.3 vs 14.2 us at K = 320, 64 tiles 20.0 vs 16.3 us at
+// K = 576).
+constexpr int kSmallTiles = 45;
 // The 16 x 16 x 128 family's choice also weighs K: k_gemm_small16 keeps one wave per 64 x 64
 // tile, so it wins while its waves are few or short.  Kernel time per launch (graph of 20
 // launches, MI355X), small16 against pipe16: 25-32 tiles 33 vs 40 us at K = 4096; 36-48 tiles
@@ -1510,14 +1511,15 @@ hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64
 // 256 (two 128-byte steps; each further step adds a memory round trip that the one-launch
 // kernel does not hide: measured through the C ABI, 10.8 against 9.6 us at [128, 256, 512],
 // 35 against 16 us at K = 2048), at most 256 blocks of 64 x 64 (one per CU: 7.7 against 8.5 us
-// at [1024, 1024, 256], 10.2 against 9.6 us at [768, 1536, 256]), fewer than kSmallTiles tiles of
+// at [1024, 1024, 256], 10.2 against 9.6 us at [768, 1536, 256]), fewer than 40 tiles of
 // 256 x 256 (the GEMM of the two-launch form is then k_gemm_small16, whose bits it reproduces),
 // N % 16 == 0 (whole 16-byte chunks of w8_t rows), and x's transpose not asked for.
 constexpr int64_t kSmallFwdMaxBlocks = 256;
+constexpr int64_t kSmallFwdMaxTiles = 39;
 bool linear_fwd_small_ok(int64_t M, int64_t N, int64_t K, const uint8_t *x8_t) {
     if (x8_t != nullptr || M <= 0 || N <= 0 || K != kFam16K || N % 16 != 0) return false;
     if (((M + kSmallTile - 1) / kSmallTile) * ((N + kSmallTile - 1) / kSmallTile) > kSmallFwdMaxBlocks) return false;
-    return ((M + BM - 1) / BM) * ((N + BN - 1) / BN) < kSmallTiles;
+    return ((M + BM - 1) / BM) * ((N + BN - 1) / BN) <= kSmallFwdMaxTiles;
 }
 
 hipError_t launch_linear_fwd_small(const uint16_t *x, const uint16_t *w, const uint16_t *bias, int64_t M, int64_t N,
