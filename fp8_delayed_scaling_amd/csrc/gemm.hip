@@ -1508,9 +1508,9 @@ hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64
 }
 
 // The one-launch small forward applies where it beats the cast-pair launch + GEMM launch: K ==
-// 256 (two 128-byte steps; each further step adds a memory round trip that the one-launch
-// kernel does not hide: measured through the C ABI, 10.8 against 9.6 us at [128, 256, 512],
-// 35 against 16 us at K = 2048), at most 256 blocks of 64 x 64 (one per CU: 7.7 against 8.5 us
+// 256 (two 128-byte steps; each further step adds about 1.9 us of casts, code stores, barriers
+// and transpose gathers, which loading the rows two steps ahead does not shorten: measured
+// through the C ABI, 10.8 against 9.6 us at [128, 256, 512], 35 against 16 us at K = 2048), at most 256 blocks of 64 x 64 (one per CU: 7.7 against 8.5 us
 // at [1024, 1024, 256], 10.2 against 9.6 us at [768, 1536, 256]), fewer than 40 tiles of
 // 256 x 256 (the GEMM of the two-launch form is then k_gemm_small16, whose bits it reproduces),
 // N % 16 == 0 (whole 16-byte chunks of w8_t rows), and x's transpose not asked for.
