@@ -137,3 +137,20 @@ def test_gemm_random_shapes(case):
     R_rows, R_cols = oracle.gemm_bias_sampled(A8, fa, 0.5, B8, fb, 0.25, bias, rows, cols)
     gemm_close(to_f64(D[torch.from_numpy(rows).to(DEV)]), R_rows, bf16_out=(od == 0))
     gemm_close(to_f64(D[:, torch.from_numpy(cols).to(DEV)]), R_cols, bf16_out=(od == 0))
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 65536), (3, 5, 65520), (17, 33, 16448), (40, 24, 32768)])
+def test_gemm_long_k_few_outputs(shape):
+    """Long K with a handful of outputs (hundreds of K steps in one wave; K % 256 == 0, K % 64 ==
+    0 and K % 16 == 0 only): every output against the float64 oracle."""
+    M, N, K = shape
+    print(f"gemm long K M={M} N={N} K={K}", flush=True)
+    A8 = oracle.cast_amax(S.normal_bf16(S.seed_for(10, 27), (M, K), 1.0), 1.0, F.E4M3)[0]
+    B8 = oracle.cast_amax(S.normal_bf16(S.seed_for(10, 28), (N, K), 1.0), 1.0, F.E5M2)[0]
+    bias = S.normal_bf16(S.seed_for(10, 29), (N,), 0.1)
+    for od in (0, 1):
+        D = torch.full((M, N), float("nan"), device=DEV, dtype=torch.bfloat16 if od == 0 else torch.float32)
+        F.fp8_gemm_bias(torch.from_numpy(A8).to(DEV), F.E4M3, scalar(0.5), torch.from_numpy(B8).to(DEV), F.E5M2,
+                        scalar(0.25), bf16_dev(bias), D)
+        torch.cuda.synchronize()
+        gemm_close(to_f64(D), oracle.gemm_bias(A8, F.E4M3, 0.5, B8, F.E5M2, 0.25, bias), bf16_out=(od == 0))
