@@ -180,6 +180,17 @@ __device__ __forceinline__ void ct_tile_of(uint32_t block, int64_t rows, uint32_
     }
 }
 
+// Sum of 16 values as a balanced tree (adjacent pairs first), so that a column sum's rounding
+// depth grows by 4 per 16 partials instead of by 16.
+__device__ __forceinline__ float sum16_pairwise(const float (&v)[16]) {
+    float a[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] = v[2 * u] + v[2 * u + 1];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a[u] = a[2 * u] + a[2 * u + 1];
+    return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
 template <int FMT, bool VEC, bool DBIAS, int TS = kTile>
 __global__ __launch_bounds__((TS / 8) * (TS / 8)) void k_cast_transpose(const CtBatch batch, float *__restrict__ partial) {
     // TS x TS tiles: 256 (1024 threads) in general, 64 (64 threads) for tensors of few tiles
@@ -401,11 +412,11 @@ __global__ __launch_bounds__((TS / 8) * (TS / 8)) void k_cast_transpose(const Ct
 }
 
 // dbias[j] = sum over row tiles of partial[tile][j], in a fixed order: a 256-thread block owns
-// 64 columns; thread (g = t / 64, c = t % 64) sums tiles g, g + 4, g + 8, ... in increasing order,
-// then the four partial sums are added in the order g = 0, 1, 2, 3.  The order depends only on
-// the number of tiles, so the result is the same run to run.  A thread's loads go out sixteen at
-// a time before their sums (same order; the last batch's missing tiles are skipped), so it waits
-// for one memory round trip per 16 tiles instead of one per tile.
+// 64 columns; thread (g = t / 64, c = t % 64) takes tiles g, g + 4, g + 8, ... in batches of 16
+// (the last batch's missing tiles count as zero), sums each batch as a balanced tree and the
+// batch sums in increasing order; then (g0 + g1) + (g2 + g3).  The order depends only on the
+// number of tiles, so the result is the same run to run.  A thread's 16 loads go out before
+// their sums, so it waits for one memory round trip per 16 tiles instead of one per tile.
 __global__ __launch_bounds__(256) void k_dbias_reduce(const float *__restrict__ partial, int64_t ntiles,
                                                       int64_t cols, float *__restrict__ dbias) {
     __shared__ float part[4][64];
@@ -418,19 +429,18 @@ __global__ __launch_bounds__(256) void k_dbias_reduce(const float *__restrict__ 
             float v[16];
 #pragma unroll
             for (int u = 0; u < 16; ++u) v[u] = i + 4 * u < ntiles ? p[(i + 4 * u) * cols] : 0.f;
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-                if (i + 4 * u < ntiles) acc += v[u];
+            acc += sum16_pairwise(v);
         }
     }
     part[g][c] = acc;
     __syncthreads();
-    if (g == 0 && j < cols) dbias[j] = ((part[0][c] + part[1][c]) + part[2][c]) + part[3][c];
+    if (g == 0 && j < cols) dbias[j] = (part[0][c] + part[1][c]) + (part[2][c] + part[3][c]);
 }
 
 // ------------------------------------------------------------------------------------------
 // dbias + cast + transpose in one launch, for tensors of whole 256 x 256 tiles that take at
-// most two tiles per CU (the bias gradient of a narrow layer, e.g. dy [8192, 4096]: 512 tiles).
+// most two tiles per CU, or three or four evenly (the bias gradient of a narrow layer, e.g. dy
+// [8192, 4096]: 512 tiles; [8192, 8192]: 1024).
 // With that few tiles the two-kernel form above pays twice for ramp-up and drain (two waves of
 // blocks, then the reduction launch); here one block per CU works through the row tiles of one
 // 256-column strip, and the column sums are finished inside the same launch:
@@ -444,8 +454,9 @@ __global__ __launch_bounds__(256) void k_dbias_reduce(const float *__restrict__ 
 //   * before its last tile's stores, a block publishes its partials (agent-scope atomic stores,
 //     coherent across the XCDs' L2 caches, complete before the next step) and adds one to its
 //     strip's counter (a relaxed agent-scope atomic add); the block that brings the count to
-//     nslots sums the strip's nslots partials in slot order into dbias (agent-scope atomic
-//     loads) and sets the counter back to zero.
+//     nslots sums the strip's nslots partials into dbias (agent-scope atomic loads; batches of
+//     16 slots, each a balanced tree, the batch sums in slot order) and sets the counter back
+//     to zero.
 // The result does not depend on which block comes last, so it is the same run to run.  The
 // counters live at the start of the workspace: zero before the first call, and every call
 // leaves them zero.  Measured on the same buffers at [8192, 4096], cold: 24.7 us (68% of
@@ -458,12 +469,19 @@ constexpr int kMaxStrips = (int)(kStripCounterBytes / 4);
 static_assert(kStripCounterBytes == (int64_t)FP8DS_DBIAS_COUNTER_BYTES, "header and library agree");
 
 // Slots per strip for the one-launch form, or 0 when the tensor takes the two-kernel form.
+// Up to two tiles per block always; three or four only when every block gets the same number
+// (tiles_r a multiple of the slots) and there are at least 16 strips.  Measured on the same
+// buffers, cold, against the two-kernel form: [8192, 8192] 54.5 against 64.2 us (four tiles per
+// block), [12288, 4096] 37.9 against 41.4 us (three); with blocks of unequal work ([8192, 6144],
+// [4096, 12288]) or few wide strips ([32768, 2048]) the two-kernel form is 1-4% faster.
+constexpr int64_t kStripMinStripsDeep = 16;
 static int dbias_strip_slots(int64_t rows, int64_t cols) {
     if (rows <= 0 || cols <= 0 || rows % kTile != 0 || cols % kTileC != 0) return 0;
     const int64_t tiles_r = rows / kTile, tiles_c = cols / kTileC;
-    if (tiles_c > kMaxStrips || tiles_r * tiles_c > 2 * kStripBlocks) return 0;
+    if (tiles_c > kMaxStrips || tiles_r * tiles_c > 4 * kStripBlocks) return 0;
     const int64_t ns = std::min<int64_t>(tiles_r, kStripBlocks / tiles_c);
-    if (ns < 1 || 2 * ns < tiles_r) return 0;          // at most two tiles per block
+    if (ns < 1 || 4 * ns < tiles_r) return 0;                   // at most four tiles per block
+    if (2 * ns < tiles_r && (tiles_r % ns != 0 || tiles_c < kStripMinStripsDeep)) return 0;
     return (int)ns;
 }
 
@@ -633,9 +651,7 @@ __global__ __launch_bounds__(kCtThreads) void k_dbias_strips(const uint16_t *__r
                     v[u] = i + u < nslots ? __hip_atomic_load(p + (int64_t)(i + u) * cols, __ATOMIC_RELAXED,
                                                               __HIP_MEMORY_SCOPE_AGENT)
                                           : 0.f;
-#pragma unroll
-                for (int u = 0; u < 16; ++u)
-                    if (i + u < nslots) acc += v[u];
+                acc += sum16_pairwise(v);
             }
             dbias[c0 + t] = acc;
         }

@@ -128,8 +128,9 @@ size_t fp8_dbias_workspace_bytes(int64_t rows, int64_t cols);
  * it); every call leaves them zero again, so the workspace stays valid for later calls and
  * graph replays of any shape.  The rest of it needs no initialisation.  Calls that overlap in
  * time must not share a workspace.  Tensors of whole 256 x 256 tiles that give each CU at most
- * two tiles run as one launch that finishes dbias itself (through those counters); all others
- * as the tile kernel plus a reduction launch.  No noop flag (dy is new every iteration).
+ * two tiles (or three or four, the same number for every CU, with at least 16 tile columns) run
+ * as one launch that finishes dbias itself (through those counters); all others as the tile
+ * kernel plus a reduction launch.  No noop flag (dy is new every iteration).
  */
 int fp8_dbias_cast_transpose(const uint16_t *dy, int64_t rows, int64_t cols, const float *scale,
                              int fmt, uint8_t *out, uint8_t *out_t, float *scale_inv_out,

@@ -72,3 +72,14 @@ def oracle_cast_transpose_rows(oracle, x, scale, fmt, nthreads=16, with_dbias=Fa
     amax = max(np.float32(p[2]) for p in parts)
     db = sum(p[4] for p in parts) if with_dbias else None
     return q, qt, np.float32(amax), parts[0][3], db
+
+
+def kernel_names(fn):
+    """Names of the GPU kernels ``fn`` launches (torch's profiler), or None when it records none."""
+    from torch.profiler import ProfilerActivity, profile
+    torch.cuda.synchronize()
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        fn()
+        torch.cuda.synchronize()
+    names = [e.name for e in prof.events() if e.device_type == torch.autograd.DeviceType.CUDA]
+    return names or None

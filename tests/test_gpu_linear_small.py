@@ -11,7 +11,7 @@ import torch
 import fp8_delayed_scaling_amd as F
 import oracle
 import synthetic as S
-from helpers import DEV, bf16_dev, f32_bits, gemm_close, to_f64, u8_host
+from helpers import DEV, bf16_dev, f32_bits, gemm_close, kernel_names, to_f64, u8_host
 
 pytestmark = pytest.mark.gpu
 
@@ -148,17 +148,6 @@ def test_one_launch_cached_weight_and_graph():
         gemm_close(to_f64(a.y), fw["y"], bf16_out=True)
 
 
-def _kernel_names(fn):
-    """Names of the GPU kernels ``fn`` launches (torch's profiler), or None when it records none."""
-    from torch.profiler import ProfilerActivity, profile
-    torch.cuda.synchronize()
-    with profile(activities=[ProfilerActivity.CUDA]) as prof:
-        fn()
-        torch.cuda.synchronize()
-    names = [e.name for e in prof.events() if e.device_type == torch.autograd.DeviceType.CUDA]
-    return names or None
-
-
 @pytest.mark.parametrize("shape, one", [((128, 256, 256), True), ((1024, 1024, 256), True), ((128, 256, 512), False),
                                         ((768, 1536, 256), False)])
 def test_dispatch_rule_launches(shape, one):
@@ -170,7 +159,7 @@ def test_dispatch_rule_launches(shape, one):
     scales = torch.tensor([2.0, 48.0], **F32)
     o = Fwd(M, N, K)
     _layer_call(x, w, None, scales, o)
-    names = _kernel_names(lambda: _layer_call(x, w, None, scales, o))
+    names = kernel_names(lambda: _layer_call(x, w, None, scales, o))
     if names is None:
         pytest.skip("the profiler recorded no GPU kernels on this build")
     fp8 = [n for n in names if "fp8ds" in n]

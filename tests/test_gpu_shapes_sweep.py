@@ -1,7 +1,7 @@
 """Seeded random shapes through the size-dependent code paths: cast+transpose (64 x 64 tiles below
 128 tiles of 256 x 256, else 256 x 256; the 16-byte path and the element-wise path), dbias + cast
 + transpose (the one-launch strip form for tensors of whole tiles with at most two tiles per CU,
-else the tile kernel + reduction), and the forward of a layer (one launch for small layers,
+or three or four evenly, else the tile kernel + reduction), and the forward of a layer (one launch for small layers,
 else the cast launch + GEMM), and the GEMM (both MFMA families, small-problem and 256 x 256
 kernels, all format pairs, bfloat16 and float32 output).  Every code, transpose, amax and
 inverse scale against the oracle bit for bit; dbias, y and D within their bounds."""
@@ -12,7 +12,7 @@ import torch
 import fp8_delayed_scaling_amd as F
 import oracle
 import synthetic as S
-from helpers import DEV, bf16_dev, f32_bits, gemm_close, scalar, to_f64, u8_host
+from helpers import DEV, bf16_dev, f32_bits, gemm_close, kernel_names, scalar, to_f64, u8_host
 
 pytestmark = pytest.mark.gpu
 
@@ -47,12 +47,15 @@ def test_cast_transpose_random_shapes(shape):
 
 def _dbias_shapes():
     # whole-tile shapes: tiles_r in [1, 32], tiles_c in [1, 40], some with at most 512 tiles and
-    # two tiles per CU (strip form), some beyond (tile kernel); plus ragged shapes
+    # two tiles per CU (strip form), some beyond (tile kernel); whole-tile shapes with three or
+    # four tiles per CU, even (strip form) and uneven or with few strips (tile kernel); plus
+    # ragged shapes
     tr = _draw(S.seed_for(10, 3), 6, 1, 32)
     tc = _draw(S.seed_for(10, 4), 6, 1, 40)
     whole = [(256 * a, 256 * b) for a, b in zip(tr, tc)]
+    deep = [(8192, 8192), (12288, 4096), (1024, 65536), (8192, 6144), (32768, 2048), (768, 65536)]
     ragged = list(zip(_draw(S.seed_for(10, 5), 3, 1, 5000), _draw(S.seed_for(10, 6), 3, 1, 3000)))
-    return whole + ragged
+    return whole + deep + ragged
 
 
 @pytest.mark.parametrize("shape", _dbias_shapes())
@@ -66,15 +69,44 @@ def test_dbias_random_shapes(shape):
     db = torch.full((C,), float("nan"), dtype=torch.float32, device=DEV)
     ws = torch.zeros(F.fp8_dbias_workspace_bytes(R, C), dtype=torch.uint8, device=DEV)
     sinv, slot = scalar(-1.0), scalar(0.0)
+    rq, rqt, ra, rs, rdb = oracle.dbias_cast_transpose(dyh, 2048.0, F.E5M2)
     for rep in range(2):                      # the second call reuses the workspace as left
         F.fp8_dbias_cast_transpose(dy, scalar(2048.0), F.E5M2, out, out_t, db, ws, sinv, slot)
         torch.cuda.synchronize()
-        rq, rqt, ra, rs, rdb = oracle.dbias_cast_transpose(dyh, 2048.0, F.E5M2)
         assert np.array_equal(u8_host(out), rq) and np.array_equal(u8_host(out_t), rqt), rep
         assert f32_bits(slot.item()) == f32_bits(ra) and f32_bits(sinv.item()) == f32_bits(rs), rep
         bound = 1e-5 * np.abs(S.bf16_bits_to_f64(dyh)).sum(axis=0) + 1e-30
         assert np.all(np.abs(db.cpu().numpy().astype(np.float64) - rdb) <= bound), rep
         assert not torch.any(ws[:1024]), rep
+
+
+@pytest.mark.parametrize("shape, strips", [((8192, 4096), True), ((8192, 8192), True), ((12288, 4096), True),
+                                           ((768, 65536), True), ((8192, 6144), False), ((32768, 2048), False),
+                                           ((4096, 12288), False), ((8448, 4096), False)])
+def test_dbias_dispatch_rule_launches(shape, strips):
+    """Whole-tile tensors with at most two tiles per CU, or three or four per CU for every CU
+    with at least 16 tile columns, run as the single k_dbias_strips launch; the others as the
+    tile kernel + k_dbias_reduce (the same codes either way; this checks which one ran)."""
+    R, C = shape
+    dy = bf16_dev(S.normal_bf16(S.seed_for(10, 30), shape, 0.01))
+    out = torch.empty((R, C), dtype=torch.uint8, device=DEV)
+    out_t = torch.empty((C, R), dtype=torch.uint8, device=DEV)
+    db = torch.empty((C,), dtype=torch.float32, device=DEV)
+    ws = torch.zeros(F.fp8_dbias_workspace_bytes(R, C), dtype=torch.uint8, device=DEV)
+    sinv, slot, sc = scalar(0.0), scalar(0.0), scalar(2048.0)
+    call = lambda: F.fp8_dbias_cast_transpose(dy, sc, F.E5M2, out, out_t, db, ws, sinv, slot)
+    call()
+    names = kernel_names(call)
+    if names is None:
+        pytest.skip("the profiler recorded no GPU kernels on this build")
+    fp8 = [n for n in names if "fp8ds" in n]
+    print(f"dbias dispatch {shape}: {fp8}", flush=True)
+    if strips:
+        assert len(fp8) == 1 and "k_dbias_strips" in fp8[0]
+    else:
+        assert len(fp8) == 2 and not any("k_dbias_strips" in n for n in fp8)
+        assert "k_dbias_reduce" in fp8[1]
+    assert not torch.any(ws[:1024])
 
 
 def _fwd_shapes():
