@@ -2,8 +2,8 @@
 workspace entry point (fp8_dbias_cast_transpose) and the oracle, called through the C ABI.
 
 Two calls in a row on the library's static scratch, the second with a smaller input (the
-scratch then still holds the first call's partials), at the backward-prep shape [8192, 4096]
-and a ragged one; every output must equal the workspace entry point's bit for bit (same
+scratch then still holds the first call's partials), at the backward-prep shape [8192, 4096],
+at shapes that give each CU four and three tiles in the one-launch form, and at ragged shapes; every output must equal the workspace entry point's bit for bit (same
 kernels, same summation order), and the codes, amax and inverse scale the oracle's."""
 import ctypes
 
@@ -62,7 +62,7 @@ def _one(shape, seed):
     assert np.all(np.abs(db.cpu().numpy().astype(np.float64) - dbr) <= bound)
 
 
-@pytest.mark.parametrize("shapes", [((8192, 4096), (2048, 1024)), ((1300, 777), (260, 136))])
+@pytest.mark.parametrize("shapes", [((8192, 4096), (2048, 1024)), ((8192, 8192), (12288, 4096)), ((1300, 777), (260, 136))])
 def test_noalloc_two_calls_second_smaller(shapes):
     big, small = shapes
     _one(big, S.seed_for(3, 12))
