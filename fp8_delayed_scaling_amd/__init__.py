@@ -145,6 +145,15 @@ def _want(t, dtypes, name, contiguous=True, shape=None, min_numel=None, required
         raise ValueError(f"{name} must hold at least {min_numel} elements, got {t.numel()}")
 
 
+def _workspace_bytes(workspace) -> int:
+    """Size of a dbias workspace tensor in bytes (0 for None); it must be one dense block."""
+    if workspace is None:
+        return 0
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return workspace.numel() * workspace.element_size()
+
+
 def _scalars(**kw):
     """float32 device scalars (scale, inverse scale, amax slot, noop flag): one element each."""
     for name, t in kw.items():
@@ -190,10 +199,8 @@ def fp8_dbias_cast_transpose(dy, scale, fmt, out, out_t, dbias, workspace, scale
     _want(dbias, _F32, "dbias", shape=(C,), required=True)
     _want(out, _U8, "out", shape=(R, C))
     _want(out_t, _U8, "out_t", shape=(C, R))
-    if isinstance(workspace, torch.Tensor) and not workspace.is_contiguous():
-        raise ValueError("workspace must be contiguous")
+    ws_bytes = _workspace_bytes(workspace)
     _scalars(scale=scale, scale_inv_out=scale_inv_out, amax_slot=amax_slot)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().fp8_dbias_cast_transpose(_ptr(dy), R, C, _ptr(scale), int(fmt), _ptr(out), _ptr(out_t),
                                           _ptr(scale_inv_out), _ptr(amax_slot), _ptr(dbias), _ptr(workspace),
                                           ws_bytes, _stream(stream)))
@@ -343,9 +350,9 @@ def fp8_linear_bwd(dy, K, dy_scale, dy_amax, dy8, dy8_t, dy_scale_inv, dbias, wo
     _want(w8_t, _U8, "w8_t", shape=(K, N), required=True)
     _want(dx, (torch.bfloat16,), "dx", shape=(M, K), required=True)
     _want(dw, (torch.bfloat16, torch.float32), "dw", shape=(N, K), required=True)
+    ws_bytes = _workspace_bytes(workspace)
     _scalars(dy_scale=dy_scale, dy_amax=dy_amax, dy_scale_inv=dy_scale_inv, x_scale_inv=x_scale_inv,
              w_scale_inv=w_scale_inv)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().fp8_linear_bwd(_ptr(dy), M, N, int(K), _ptr(dy_scale), _ptr(dy_amax), _ptr(dy8), _ptr(dy8_t),
                                 _ptr(dy_scale_inv), _ptr(dbias), _ptr(workspace), ws_bytes, _ptr(x8_t),
                                 _ptr(x_scale_inv), _ptr(w8_t), _ptr(w_scale_inv), _ptr(dx), _ptr(dw),

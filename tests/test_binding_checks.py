@@ -46,6 +46,8 @@ def test_dbias_checks():
     _raises("dbias", F.fp8_dbias_cast_transpose, dy, s, F.E5M2, out, out_t, torch.empty(16, dtype=torch.float16), ws)
     _raises("out_t", F.fp8_dbias_cast_transpose, dy, s, F.E5M2, out, torch.empty((32, 16), **u8),
             torch.empty(16, **f32), ws)
+    _raises("workspace", F.fp8_dbias_cast_transpose, dy, s, F.E5M2, out, out_t, torch.empty(16, **f32),
+            torch.empty((64, 128), **u8)[:, ::2])
 
 
 def test_scale_update_checks():
@@ -111,6 +113,7 @@ def _bwd_args(M=32, N=48, K=64):
     ("dw", torch.empty((48, 63), **f32)),
     ("dw", torch.empty((48, 64), dtype=torch.float16)),
     ("dy_scale_inv", torch.empty(0, **f32)),
+    ("workspace", torch.empty((256, 512), **u8)[:, ::2]),
 ])
 def test_linear_bwd_checks(name, bad):
     a = _bwd_args()
