@@ -522,6 +522,15 @@ def extras(F, S, torch, np, dev, bf16, step):
         L.fp8_linear_fwd(*raw_args)
     torch.cuda.synchronize()
     raw_us = (time.perf_counter() - t) / 200 * 1e6
+    # the binding's prepared call: checks and marshalling once, then only the C call per call
+    prep = F.prepare(small_fwd)
+    prep()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(200):
+        prep()
+    torch.cuda.synchronize()
+    prepared_us = (time.perf_counter() - t) / 200 * 1e6
     # the captured graph launched with hipGraphLaunch itself (what a C caller replaying it pays,
     # without torch's replay bookkeeping); the HIP runtime is the one torch already loaded
     hip_graph_us = None
@@ -541,6 +550,7 @@ def extras(F, S, torch, np, dev, bf16, step):
         pass
     out["small_forward_128x256x256"] = {"eager_us_per_call": round(eager_us, 2), "graph_replay_us": round(graph_us, 2),
                                         "c_abi_eager_us_per_call": round(raw_us, 2),
+                                        "prepared_us_per_call": round(prepared_us, 2),
                                         "hip_graph_launch_us": hip_graph_us, "launches": 1}
 
     # N-chunked GEMM + bias, M=8192, K=N=12288 (x8 and the first 12288 rows of W8), one stream

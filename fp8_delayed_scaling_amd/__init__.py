@@ -14,6 +14,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import threading
 from typing import Optional, Sequence
 
 import torch
@@ -23,7 +24,7 @@ __all__ = [
     "fp8ds_status_string", "fp8ds_version",
     "fp8_cast_amax", "fp8_cast_transpose", "fp8_dbias_workspace_bytes", "fp8_dbias_cast_transpose",
     "fp8_dbias_cast_transpose_noalloc", "fp8_scale_update", "fp8_gemm_bias", "fp8_gemm_bias_chunked", "fp8_gemm_bias_fp8", "fp8_transpose",
-    "fp8_linear_fwd", "fp8_linear_bwd",
+    "fp8_linear_fwd", "fp8_linear_bwd", "prepare", "Prepared",
 ]
 
 E4M3 = 0
@@ -118,6 +119,54 @@ def _check(status: int):
         raise Fp8dsError(status, fp8ds_status_string(status))
 
 
+_tls = threading.local()   # .rec: the list prepare() records into, on this thread only
+
+
+def _invoke(name: str, *cargs):
+    """Call entry point ``name`` with marshalled arguments, or hand them to prepare()."""
+    rec = getattr(_tls, "rec", None)
+    if rec is not None:
+        rec.append((name, cargs))
+        return
+    _check(getattr(lib(), name)(*cargs))
+
+
+class Prepared:
+    """One entry-point call whose checks and marshalling ran once, in prepare(): calling it
+    repeats only the C call, with the same device pointers, sizes and stream (or ``stream``).
+    It keeps the tensors it was prepared with alive; they must keep their storage (no resize,
+    no set_) for as long as it is used."""
+
+    def __init__(self, name: str, cargs, keep):
+        self.name = name
+        self._fn = getattr(lib(), name)
+        self._args = tuple(cargs)
+        self._keep = keep
+
+    def __call__(self, stream=None):
+        a = self._args if stream is None else self._args[:-1] + (_stream(stream),)
+        status = self._fn(*a)
+        if status != 0:
+            raise Fp8dsError(status, fp8ds_status_string(status))
+
+
+def prepare(fn, *args, **kwargs) -> Prepared:
+    """Run the binding ``fn`` (one of the entry points above) on these arguments up to the C call
+    and return that call, ready to repeat: for layers small enough that the binding's per-call
+    checks cost more host time than the launch itself.  The stream is the one ``fn`` would have
+    used (the current stream unless ``stream=`` is given) unless the call passes another."""
+    rec = []
+    _tls.rec = rec
+    try:
+        fn(*args, **kwargs)
+    finally:
+        _tls.rec = None
+    if len(rec) != 1:
+        raise ValueError(f"{getattr(fn, '__name__', fn)} is not a single library call")
+    name, cargs = rec[0]
+    return Prepared(name, cargs, (args, kwargs))
+
+
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
 
 
@@ -169,8 +218,8 @@ def fp8_cast_amax(x, scale, fmt, out, scale_inv_out=None, amax_slot=None, noop=N
     if out.numel() != x.numel():
         raise ValueError("out must have x's number of elements")
     _scalars(scale=scale, scale_inv_out=scale_inv_out, amax_slot=amax_slot, noop=noop)
-    _check(lib().fp8_cast_amax(_ptr(x), x.numel(), _ptr(scale), int(fmt), _ptr(out), _ptr(scale_inv_out),
-                               _ptr(amax_slot), _ptr(noop), _stream(stream)))
+    _invoke("fp8_cast_amax", _ptr(x), x.numel(), _ptr(scale), int(fmt), _ptr(out), _ptr(scale_inv_out),
+                               _ptr(amax_slot), _ptr(noop), _stream(stream))
 
 
 def fp8_cast_transpose(x, scale, fmt, out, out_t, scale_inv_out=None, amax_slot=None, noop=None, stream=None):
@@ -180,8 +229,8 @@ def fp8_cast_transpose(x, scale, fmt, out, out_t, scale_inv_out=None, amax_slot=
     _want(out, _U8, "out", shape=(R, C), required=True)
     _want(out_t, _U8, "out_t", shape=(C, R), required=True)
     _scalars(scale=scale, scale_inv_out=scale_inv_out, amax_slot=amax_slot, noop=noop)
-    _check(lib().fp8_cast_transpose(_ptr(x), R, C, _ptr(scale), int(fmt), _ptr(out), _ptr(out_t),
-                                    _ptr(scale_inv_out), _ptr(amax_slot), _ptr(noop), _stream(stream)))
+    _invoke("fp8_cast_transpose", _ptr(x), R, C, _ptr(scale), int(fmt), _ptr(out), _ptr(out_t),
+                                    _ptr(scale_inv_out), _ptr(amax_slot), _ptr(noop), _stream(stream))
 
 
 def fp8_dbias_workspace_bytes(rows: int, cols: int) -> int:
@@ -201,9 +250,9 @@ def fp8_dbias_cast_transpose(dy, scale, fmt, out, out_t, dbias, workspace, scale
     _want(out_t, _U8, "out_t", shape=(C, R))
     ws_bytes = _workspace_bytes(workspace)
     _scalars(scale=scale, scale_inv_out=scale_inv_out, amax_slot=amax_slot)
-    _check(lib().fp8_dbias_cast_transpose(_ptr(dy), R, C, _ptr(scale), int(fmt), _ptr(out), _ptr(out_t),
+    _invoke("fp8_dbias_cast_transpose", _ptr(dy), R, C, _ptr(scale), int(fmt), _ptr(out), _ptr(out_t),
                                           _ptr(scale_inv_out), _ptr(amax_slot), _ptr(dbias), _ptr(workspace),
-                                          ws_bytes, _stream(stream)))
+                                          ws_bytes, _stream(stream))
 
 
 def fp8_dbias_cast_transpose_noalloc(dy, scale, fmt, out, out_t, dbias, scale_inv_out=None, amax_slot=None,
@@ -216,9 +265,9 @@ def fp8_dbias_cast_transpose_noalloc(dy, scale, fmt, out, out_t, dbias, scale_in
     _want(out, _U8, "out", shape=(R, C))
     _want(out_t, _U8, "out_t", shape=(C, R))
     _scalars(scale=scale, scale_inv_out=scale_inv_out, amax_slot=amax_slot)
-    _check(lib().fp8_dbias_cast_transpose_noalloc(_ptr(dy), R, C, _ptr(scale), int(fmt), _ptr(out), _ptr(out_t),
+    _invoke("fp8_dbias_cast_transpose_noalloc", _ptr(dy), R, C, _ptr(scale), int(fmt), _ptr(out), _ptr(out_t),
                                                   _ptr(scale_inv_out), _ptr(amax_slot), _ptr(dbias),
-                                                  _stream(stream)))
+                                                  _stream(stream))
 
 
 def fp8_scale_update(amax_history, scale, scale_inv, fmts: Sequence[int], margin: int = 0, stream=None):
@@ -230,8 +279,8 @@ def fp8_scale_update(amax_history, scale, scale_inv, fmts: Sequence[int], margin
     if len(fmts) != T:
         raise ValueError("one format per tensor")
     f = (ctypes.c_int32 * T)(*[int(v) for v in fmts])
-    _check(lib().fp8_scale_update(_ptr(amax_history), L, T, _ptr(scale), _ptr(scale_inv),
-                                  ctypes.cast(f, ctypes.c_void_p), int(margin), _stream(stream)))
+    _invoke("fp8_scale_update", _ptr(amax_history), L, T, _ptr(scale), _ptr(scale_inv),
+                                  ctypes.cast(f, ctypes.c_void_p), int(margin), _stream(stream))
 
 
 def _out_dtype(D):
@@ -262,7 +311,7 @@ def _gemm_args(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D):
 
 def fp8_gemm_bias(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D, stream=None):
     """D = (A B^T) * a_scale_inv * b_scale_inv + bias, A [M, K] and B [N, K] FP8 codes."""
-    _check(lib().fp8_gemm_bias(*_gemm_args(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D), _stream(stream)))
+    _invoke("fp8_gemm_bias", *_gemm_args(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D), _stream(stream))
 
 
 def fp8_gemm_bias_fp8(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D, d_fmt, d_scale, d_scale_inv_out=None,
@@ -284,10 +333,10 @@ def fp8_gemm_bias_fp8(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D, d_fmt, d_
     for t, nm in ((A, "A"), (B, "B"), (D, "D")):
         if t.numel() and t.stride(1) != 1:
             raise ValueError(f"{nm} rows must be contiguous")
-    _check(lib().fp8_gemm_bias_fp8(_ptr(A), int(fa), _ptr(a_scale_inv), A.stride(0), _ptr(B), int(fb),
+    _invoke("fp8_gemm_bias_fp8", _ptr(A), int(fa), _ptr(a_scale_inv), A.stride(0), _ptr(B), int(fb),
                                    _ptr(b_scale_inv), B.stride(0), _ptr(bias), _ptr(D), D.stride(0), int(d_fmt),
                                    _ptr(d_scale), _ptr(d_scale_inv_out), _ptr(d_amax_slot), M, N, K,
-                                   _stream(stream)))
+                                   _stream(stream))
 
 
 def fp8_transpose(x8, out_t, noop=None, stream=None):
@@ -296,7 +345,7 @@ def fp8_transpose(x8, out_t, noop=None, stream=None):
     R, C = x8.shape
     _want(out_t, _U8, "out_t", shape=(C, R), required=True)
     _scalars(noop=noop)
-    _check(lib().fp8_transpose(_ptr(x8), R, C, _ptr(out_t), _ptr(noop), _stream(stream)))
+    _invoke("fp8_transpose", _ptr(x8), R, C, _ptr(out_t), _ptr(noop), _stream(stream))
 
 
 def fp8_gemm_bias_chunked(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D, n_chunks: int,
@@ -307,9 +356,9 @@ def fp8_gemm_bias_chunked(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D, n_chu
         if len(chunk_streams) < n_chunks:
             raise ValueError("one stream per chunk")
         arr = (ctypes.c_void_p * n_chunks)(*[_stream(s) for s in chunk_streams[:n_chunks]])
-    _check(lib().fp8_gemm_bias_chunked(*_gemm_args(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D),
+    _invoke("fp8_gemm_bias_chunked", *_gemm_args(A, fa, a_scale_inv, B, fb, b_scale_inv, bias, D),
                                        int(n_chunks), None if arr is None else ctypes.cast(arr, ctypes.c_void_p),
-                                       _stream(stream)))
+                                       _stream(stream))
 
 
 def fp8_linear_fwd(x, w, bias, x_scale, x_amax, x8, x8_t, x_scale_inv, w_scale, w_amax, w8, w8_t, w_scale_inv,
@@ -329,9 +378,9 @@ def fp8_linear_fwd(x, w, bias, x_scale, x_amax, x8, x8_t, x_scale_inv, w_scale, 
     _want(w8_t, _U8, "w8_t", shape=(K, N), required=True)
     _scalars(x_scale=x_scale, x_amax=x_amax, x_scale_inv=x_scale_inv, w_scale=w_scale, w_amax=w_amax,
              w_scale_inv=w_scale_inv, w_noop=w_noop)
-    _check(lib().fp8_linear_fwd(_ptr(x), _ptr(w), _ptr(bias), M, N, K, _ptr(x_scale), _ptr(x_amax), _ptr(x8),
+    _invoke("fp8_linear_fwd", _ptr(x), _ptr(w), _ptr(bias), M, N, K, _ptr(x_scale), _ptr(x_amax), _ptr(x8),
                                 _ptr(x8_t), _ptr(x_scale_inv), _ptr(w_scale), _ptr(w_amax), _ptr(w8), _ptr(w8_t),
-                                _ptr(w_scale_inv), _ptr(w_noop), _ptr(y), _stream(stream)))
+                                _ptr(w_scale_inv), _ptr(w_noop), _ptr(y), _stream(stream))
 
 
 def fp8_linear_bwd(dy, K, dy_scale, dy_amax, dy8, dy8_t, dy_scale_inv, dbias, workspace, x8_t, x_scale_inv, w8_t,
@@ -353,7 +402,7 @@ def fp8_linear_bwd(dy, K, dy_scale, dy_amax, dy8, dy8_t, dy_scale_inv, dbias, wo
     ws_bytes = _workspace_bytes(workspace)
     _scalars(dy_scale=dy_scale, dy_amax=dy_amax, dy_scale_inv=dy_scale_inv, x_scale_inv=x_scale_inv,
              w_scale_inv=w_scale_inv)
-    _check(lib().fp8_linear_bwd(_ptr(dy), M, N, int(K), _ptr(dy_scale), _ptr(dy_amax), _ptr(dy8), _ptr(dy8_t),
+    _invoke("fp8_linear_bwd", _ptr(dy), M, N, int(K), _ptr(dy_scale), _ptr(dy_amax), _ptr(dy8), _ptr(dy8_t),
                                 _ptr(dy_scale_inv), _ptr(dbias), _ptr(workspace), ws_bytes, _ptr(x8_t),
                                 _ptr(x_scale_inv), _ptr(w8_t), _ptr(w_scale_inv), _ptr(dx), _ptr(dw),
-                                _out_dtype(dw), _stream(stream)))
+                                _out_dtype(dw), _stream(stream))

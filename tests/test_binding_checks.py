@@ -128,3 +128,13 @@ def test_well_formed_host_call_fails_only_at_the_pointer_step():
         F.fp8_linear_fwd(**_fwd_args())
     with pytest.raises(ValueError, match="must live on the GPU"):
         F.fp8_linear_bwd(**_bwd_args())
+
+
+def test_prepare_needs_one_library_call():
+    """prepare() records exactly one C call; a function that makes none is refused, and a failed
+    check inside it leaves the binding in its normal (calling) state."""
+    with pytest.raises(ValueError, match="not a single library call"):
+        F.prepare(lambda: None)
+    with pytest.raises((ValueError, TypeError), match="out_t"):
+        F.prepare(F.fp8_transpose, torch.empty((8, 16), **u8), torch.empty((8, 16), **u8))
+    assert getattr(F._tls, "rec", None) is None
