@@ -283,8 +283,9 @@ def test_dbias_workspace_garbage_reuse_and_graph(shape):
 
 # Shapes of whole 256 x 256 tiles that take the one-launch strip form: one tile per block
 # ([256, 256], [768, 512], [4096, 4096]), two per block ([8192, 4096]; [2560, 12288]: 48 strips x
-# 5 slots = 240 blocks for 10 row tiles; [512, 65536]: 256 strips, every counter in use).
-@pytest.mark.parametrize("shape", [(256, 256), (768, 512), (4096, 4096), (2560, 12288), (512, 65536)])
+# 5 slots = 240 blocks for 10 row tiles; [512, 65536]: 256 strips, every counter in use), four
+# per block ([4096, 16384]: 64 strips x 4 slots).
+@pytest.mark.parametrize("shape", [(256, 256), (768, 512), (4096, 4096), (2560, 12288), (512, 65536), (4096, 16384)])
 @pytest.mark.parametrize("fmt", [1, 0])
 def test_dbias_strip_form_parity(shape, fmt):
     print(f"dbias strip form {shape} fmt {fmt}", flush=True)
@@ -306,14 +307,17 @@ def test_dbias_strip_form_parity(shape, fmt):
     assert not torch.any(ws[:COUNTER_BYTES])
 
 
+@pytest.mark.parametrize("shape", [(1024, 512), (768, 65536)])
 @pytest.mark.parametrize("scale", [2.0 ** 10, 0.0, float("inf")])
-def test_dbias_strip_form_specials(scale):
-    """Infinities, NaNs and saturating values in a strip-form tensor, and scales that are not
-    plain (zero, infinite): the exact path re-reads the rows; codes, amax and inverse scale
-    must equal the oracle's; dbias is checked where the column holds no non-finite value."""
-    R, C = 1024, 512
+def test_dbias_strip_form_specials(scale, shape):
+    """Infinities, NaNs and saturating values in a strip-form tensor (one tile per block, and
+    three per block at [768, 65536]), and scales that are not plain (zero, infinite): the exact
+    path re-reads the rows; codes, amax and inverse scale must equal the oracle's; dbias is
+    checked where the column holds no non-finite value."""
+    R, C = shape
+    print(f"dbias strip form specials {shape} scale {scale}", flush=True)
     dyh = S.normal_bf16(S.seed_for(3, 50), (R, C), 1.0)
-    for (i, j, v) in [(3, 5, 0x7F80), (700, 5, 0xFF80), (511, 300, 0x7FC0), (1023, 511, 0x7F7F), (9, 0, 0xFF7F),
+    for (i, j, v) in [(3, 5, 0x7F80), (700, 5, 0xFF80), (511, 300, 0x7FC0), (R - 1, C - 1, 0x7F7F), (9, 0, 0xFF7F),
                       (256, 256, 0x4780)]:
         dyh[i, j] = v
     dy = bf16_dev(dyh)
