@@ -124,20 +124,6 @@ constexpr int kRowBlocks = kTile / 8;                    // 32
 // swapped when g is odd.
 __device__ __forceinline__ int t_swz(int col) { return (col >> 3) & (kRowBlocks - 1); }
 
-// 4 x 4 byte transpose: byte k of a, b, c, d is element (row 0..3, column k); o_k receives
-// column k in row order (byte 0 from a).  Two rounds of two-source byte selects.
-__device__ __forceinline__ void tr4(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t &o0, uint32_t &o1,
-                                    uint32_t &o2, uint32_t &o3) {
-    const uint32_t ab_lo = __builtin_amdgcn_perm(b, a, 0x05010400u);   // a0 b0 a1 b1
-    const uint32_t ab_hi = __builtin_amdgcn_perm(b, a, 0x07030602u);   // a2 b2 a3 b3
-    const uint32_t cd_lo = __builtin_amdgcn_perm(d, c, 0x05010400u);
-    const uint32_t cd_hi = __builtin_amdgcn_perm(d, c, 0x07030602u);
-    o0 = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u);             // a0 b0 c0 d0
-    o1 = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u);             // a1 b1 c1 d1
-    o2 = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u);
-    o3 = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);
-}
-
 // One tensor of a cast launch.  out_t == nullptr: row-major codes only (no transpose cache).
 struct CtTensor {
     const uint16_t *x;

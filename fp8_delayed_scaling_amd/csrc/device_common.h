@@ -140,4 +140,18 @@ __device__ __forceinline__ float dequant_bias(float acc, float sa, float sb, flo
     return __builtin_fmaf(acc * sa, sb, b);
 }
 
+// 4 x 4 byte transpose: byte k of a, b, c, d is element (row 0..3, column k); o_k receives
+// column k in row order (byte 0 from a).  Two rounds of two-source byte selects.
+__device__ __forceinline__ void tr4(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t &o0, uint32_t &o1,
+                                    uint32_t &o2, uint32_t &o3) {
+    const uint32_t ab_lo = __builtin_amdgcn_perm(b, a, 0x05010400u);   // a0 b0 a1 b1
+    const uint32_t ab_hi = __builtin_amdgcn_perm(b, a, 0x07030602u);   // a2 b2 a3 b3
+    const uint32_t cd_lo = __builtin_amdgcn_perm(d, c, 0x05010400u);
+    const uint32_t cd_hi = __builtin_amdgcn_perm(d, c, 0x07030602u);
+    o0 = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u);             // a0 b0 c0 d0
+    o1 = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u);             // a1 b1 c1 d1
+    o2 = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u);
+    o3 = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);
+}
+
 }  // namespace fp8ds

@@ -43,6 +43,9 @@
 //
 // k_gemm_bias (any K % 16 == 0): global -> registers -> LDS with double-buffered 128-byte K
 // slices, the K tail zero-filled.
+//
+// k_linear_fwd_small / k_linear_fwd_tiny (further down): the whole forward of a small layer
+// (casts of x and W, GEMM + bias) in one launch, with the MFMAs of k_gemm_small16.
 #include <type_traits>
 
 #include "device_common.h"
@@ -1221,6 +1224,7 @@ __global__ __launch_bounds__(64) void k_gemm_small16(const uint8_t *__restrict__
 // hardware conversion, the exact encoder for a fragment holding an inf / NaN or under a zero /
 // non-finite scale), and 1/scale is formed as the cast kernels form it.
 // ------------------------------------------------------------------------------------------
+constexpr int kTinyTile = 32;
 struct SmallFwdArgs {
     const uint16_t *x, *w, *bias;
     const float *x_scale, *w_scale, *w_noop;
@@ -1406,6 +1410,135 @@ __global__ __launch_bounds__(256) void k_linear_fwd_small(const SmallFwdArgs a) 
     }
 }
 
+// k_linear_fwd_tiny: the same forward with 32 x 32 output tiles, for the smallest layers (four
+// times the blocks of the 64 x 64 form, so the casts spread over more CUs, and no barrier
+// between K steps).  K is 256, so a
+// block casts every row it needs in one pass: threads 0-127 the tile's 32 x rows, threads
+// 128-255 its 32 W rows, each thread 64 consecutive K values (four per row); the codes go to two
+// 32 x 256-byte LDS tiles (16-byte chunk c of row r at chunk c ^ (r % 16)), the owners' codes to
+// x8 / w8; after one barrier wave w multiplies x rows 16 (w / 2) .. by W rows 16 (w % 2) .. with
+// the two 128-byte K steps of k_gemm_small16 in its order (identical y), and the blocks of tile
+// row 0 write w8_t from the W tile with 4 x 4 byte register transposes.  Each wave folds its
+// amax with one atomic (no read first: at most a few dozen blocks fold).
+__global__ __launch_bounds__(256) void k_linear_fwd_tiny(const SmallFwdArgs a) {
+    __shared__ __align__(16) uint8_t sx[kTinyTile * kFam16K];
+    __shared__ __align__(16) uint8_t sw[kTinyTile * kFam16K];
+    const int tm = blockIdx.x / a.tiles_n, tn = blockIdx.x - (blockIdx.x / a.tiles_n) * a.tiles_n;
+    const int m0 = tm * kTinyTile, n0 = tn * kTinyTile;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int M = a.M, N = a.N;
+    const bool wcached = a.w_noop != nullptr && *a.w_noop == 1.0f;
+    const float xs = *a.x_scale;
+    const float ws = *a.w_scale;
+    const float sa = 1.0f / xs;
+    const float sb = wcached ? *a.w_scale_inv : 1.0f / ws;
+    if (blockIdx.x == 0 && t == 0) {
+        *a.x_scale_inv = sa;
+        if (!wcached) *a.w_scale_inv = sb;
+    }
+    const bool own_x = tn == 0, own_w = tm == 0 && !wcached;   // block-uniform
+    // ---- casts: thread t takes operand t / 128 (x, W), row (t / 4) % 32, K values 64 (t % 4) ..
+    const bool is_w = wave >= 2;                                // wave-uniform
+    const int row = (t >> 2) & 31, q = t & 3;
+    const int grow = (is_w ? n0 : m0) + row, lim = is_w ? N : M;
+    const int64_t srow = min(grow, lim - 1);                    // rows past M / N repeat the last
+    uint8_t *lds = is_w ? sw : sx;
+    i32x8 c0, c1;
+    uint32_t mag = 0;
+    if (is_w && wcached) {
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(a.w8 + srow * kFam16K + q * 64);
+        const u32x4 v0 = p[0], v1 = p[1], v2 = p[2], v3 = p[3];
+        c0 = i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+        c1 = i32x8{(int)v2.x, (int)v2.y, (int)v2.z, (int)v2.w, (int)v3.x, (int)v3.y, (int)v3.z, (int)v3.w};
+    } else {
+        const uint16_t *src = (is_w ? a.w : a.x) + srow * kFam16K + q * 64;
+        uint32_t v0[16], v1[16];
+        load32_bf16(src, v0);
+        load32_bf16(src + 32, v1);
+        const float s = is_w ? ws : xs;
+        const bool plain = scale_is_plain(s);
+        uint32_t t0, t1;
+        c0 = cast32_e4m3(v0, s, plain, &t0);
+        c1 = cast32_e4m3(v1, s, plain, &t1);
+        mag = amax_unpack(amax_pk(t0, t1));
+    }
+    {
+        const int sw4 = row & 15;
+        u32x4 *l = reinterpret_cast<u32x4 *>(lds + row * kFam16K);
+        l[(4 * q) ^ sw4] = u32x4{(uint32_t)c0[0], (uint32_t)c0[1], (uint32_t)c0[2], (uint32_t)c0[3]};
+        l[(4 * q + 1) ^ sw4] = u32x4{(uint32_t)c0[4], (uint32_t)c0[5], (uint32_t)c0[6], (uint32_t)c0[7]};
+        l[(4 * q + 2) ^ sw4] = u32x4{(uint32_t)c1[0], (uint32_t)c1[1], (uint32_t)c1[2], (uint32_t)c1[3]};
+        l[(4 * q + 3) ^ sw4] = u32x4{(uint32_t)c1[4], (uint32_t)c1[5], (uint32_t)c1[6], (uint32_t)c1[7]};
+    }
+    const bool own = is_w ? own_w : own_x;
+    if (own && grow < lim) {
+        uint8_t *dst = (is_w ? a.w8 : a.x8) + (int64_t)grow * kFam16K + q * 64;
+        store32_codes(dst, c0);
+        store32_codes(dst + 32, c1);
+    }
+    if (own) {
+        const uint32_t m = wave_max_u32(mag);
+        if (lane == 0 && m != 0u) atomicMax(reinterpret_cast<unsigned int *>(is_w ? a.w_amax : a.x_amax), m << 16);
+    }
+    // bias of this lane's four output columns, loaded while the casts finish
+    const int r16 = lane & 15, g = lane >> 4, wm = wave >> 1, wn = wave & 1;
+    const int xrow = m0 + wm * 16 + r16, col = n0 + wn * 16 + g * 4;
+    const bool has_bias = a.bias != nullptr;
+    float bv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) bv[u] = has_bias ? __uint_as_float((uint32_t)a.bias[min(col + u, N - 1)] << 16) : 0.f;
+    __syncthreads();
+    // ---- w8_t rows k, columns n0 .. n0 + 31 from the W tile: thread t transposes the 4 x 8 byte
+    // block k = 4 (t / 4) .., n = 8 (t % 4) ..
+    if (own_w) {
+        const int n8 = (t & 3) * 8, k4 = (t >> 2) * 4;
+        uint32_t d[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int n = n8 + i;
+            d[i] = *reinterpret_cast<const uint32_t *>(sw + n * kFam16K + (((k4 >> 4) ^ (n & 15)) << 4) + (k4 & 15));
+        }
+        uint32_t o[4], p[4];
+        tr4(d[0], d[1], d[2], d[3], o[0], o[1], o[2], o[3]);
+        tr4(d[4], d[5], d[6], d[7], p[0], p[1], p[2], p[3]);
+        if (n0 + n8 < N) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<u32x2 *>(a.w8_t + (int64_t)(k4 + j) * N + n0 + n8) = u32x2{o[j], p[j]};
+        }
+    }
+    // ---- the two K steps: lane l supplies row l % 16 of its 16-row x and W slices and K bytes
+    // [32 (l / 16), +32) of each step
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        const int ch = 8 * st + 2 * g;
+        const int ra = wm * 16 + r16, rb = wn * 16 + r16;
+        const u32x4 a0 = *reinterpret_cast<const u32x4 *>(sx + ra * kFam16K + ((ch ^ r16) << 4));
+        const u32x4 a1 = *reinterpret_cast<const u32x4 *>(sx + ra * kFam16K + (((ch + 1) ^ r16) << 4));
+        const u32x4 b0 = *reinterpret_cast<const u32x4 *>(sw + rb * kFam16K + ((ch ^ r16) << 4));
+        const u32x4 b1 = *reinterpret_cast<const u32x4 *>(sw + rb * kFam16K + (((ch + 1) ^ r16) << 4));
+        const i32x8 fa = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        const i32x8 fb = i32x8{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa, acc, kE4M3, kE4M3, 0, 0, 0, 0);
+    }
+    // ---- y: lane l holds y[xrow][col + u] in element u (N % 16 == 0: the four columns are all
+    // inside or all outside)
+    if (xrow < M && col < N) {
+        float val[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) val[u] = dequant_bias(acc[u], sa, sb, bv[u]);
+        uint16_t *dst = a.y + (int64_t)xrow * N + col;
+        if ((reinterpret_cast<uintptr_t>(a.y) & 7u) == 0) {
+            *reinterpret_cast<u32x2 *>(dst) = u32x2{f32x2_to_bf16x2_rne(val[0], val[1]), f32x2_to_bf16x2_rne(val[2], val[3])};
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) dst[u] = f32_to_bf16_rne(val[u]);
+        }
+    }
+}
+
 // D = bias broadcast (K == 0): no products at all.
 template <int OUT>
 __global__ __launch_bounds__(256) void k_bias_only(const uint16_t *__restrict__ bias, void *__restrict__ D,
@@ -1515,6 +1648,10 @@ hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64
 // 256 x 256 (the GEMM of the two-launch form is then k_gemm_small16, whose bits it reproduces),
 // N % 16 == 0 (whole 16-byte chunks of w8_t rows), and x's transpose not asked for.
 constexpr int64_t kSmallFwdMaxBlocks = 256;
+// Up to this many 64 x 64 blocks the 32 x 32 tiles of k_linear_fwd_tiny are faster (through the
+// C ABI, back to back: [128, 256, 256] 4.9 against 7.1 us, [512, 1024, 256] 6.1 against 7.2 us;
+// [768, 768, 256] even, [1024, 1024, 256] 9.2 against 7.4 us).
+constexpr int64_t kTinyMaxBlocks64 = 128;
 constexpr int64_t kSmallFwdMaxTiles = 39;
 bool linear_fwd_small_ok(int64_t M, int64_t N, int64_t K, const uint8_t *x8_t) {
     if (x8_t != nullptr || M <= 0 || N <= 0 || K != kFam16K || N % 16 != 0) return false;
@@ -1532,8 +1669,15 @@ hipError_t launch_linear_fwd_small(const uint16_t *x, const uint16_t *w, const u
     a.x_amax = x_amax; a.w_amax = w_amax; a.x_scale_inv = x_scale_inv; a.w_scale_inv = w_scale_inv;
     a.x8 = x8; a.w8 = w8; a.w8_t = w8_t; a.y = y;
     a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    const int64_t blocks64 = ((M + kSmallTile - 1) / kSmallTile) * ((N + kSmallTile - 1) / kSmallTile);
+    if (blocks64 <= kTinyMaxBlocks64) {
+        a.tiles_n = (int)((N + kTinyTile - 1) / kTinyTile);
+        const unsigned grid = (unsigned)(((M + kTinyTile - 1) / kTinyTile) * a.tiles_n);
+        k_linear_fwd_tiny<<<dim3(grid), dim3(256), 0, st>>>(a);
+        return hipGetLastError();
+    }
     a.tiles_n = (int)((N + kSmallTile - 1) / kSmallTile);
-    const unsigned grid = (unsigned)(((M + kSmallTile - 1) / kSmallTile) * a.tiles_n);
+    const unsigned grid = (unsigned)blocks64;
     k_linear_fwd_small<<<dim3(grid), dim3(256), 0, st>>>(a);
     return hipGetLastError();
 }

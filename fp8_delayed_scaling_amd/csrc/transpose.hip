@@ -26,22 +26,6 @@ namespace fp8ds {
 
 namespace {
 constexpr int kTT = 256;   // tile edge (bytes)
-
-// 4 x 4 byte transpose: byte k of a, b, c, d is element (row 0..3, column k); o_k receives
-// column k in row order.  Two rounds of two-source byte merges (the compiler emits v_perm_b32).
-__device__ __forceinline__ void tr4(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t &o0, uint32_t &o1,
-                                    uint32_t &o2, uint32_t &o3) {
-    const uint32_t ab_lo = (a & 0xFFu) | ((b & 0xFFu) << 8) | ((a & 0xFF00u) << 8) | ((b & 0xFF00u) << 16);
-    const uint32_t ab_hi = ((a & 0xFF0000u) >> 16) | ((b & 0xFF0000u) >> 8) | ((a & 0xFF000000u) >> 8) |
-                           (b & 0xFF000000u);
-    const uint32_t cd_lo = (c & 0xFFu) | ((d & 0xFFu) << 8) | ((c & 0xFF00u) << 8) | ((d & 0xFF00u) << 16);
-    const uint32_t cd_hi = ((c & 0xFF0000u) >> 16) | ((d & 0xFF0000u) >> 8) | ((c & 0xFF000000u) >> 8) |
-                           (d & 0xFF000000u);
-    o0 = (ab_lo & 0xFFFFu) | (cd_lo << 16);
-    o1 = (ab_lo >> 16) | (cd_lo & 0xFFFF0000u);
-    o2 = (ab_hi & 0xFFFFu) | (cd_hi << 16);
-    o3 = (ab_hi >> 16) | (cd_hi & 0xFFFF0000u);
-}
 }  // namespace
 
 template <bool VEC>

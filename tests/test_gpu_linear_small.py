@@ -1,5 +1,6 @@
 """The one-launch forward of small layers (fp8_linear_fwd when K == 256, N % 16 == 0, no x
-transpose, at most 256 output blocks of 64 x 64 and fewer than 40 of 256 x 256) against the
+transpose, at most 256 output blocks of 64 x 64 and fewer than 40 of 256 x 256; 32 x 32 tiles up
+to 128 blocks of 64 x 64) against the
 individual calls (cast of x, cast+transpose of W, GEMM + bias: every output bit for bit) and
 against the oracle (codes, amaxes and inverse scales exact, y within the GEMM tolerance),
 including the cached-weight flag, non-finite inputs, scales that are not plain, graph replay, and
@@ -51,7 +52,8 @@ def _equal(a, b):
 
 # the small layer [128, 256] x [256, 256], a ragged M, a narrow N, a wide N, the largest block
 # count (16 x 16 blocks of 64 x 64); then layers outside the rule: K = 512 and 8192, 288 blocks
-@pytest.mark.parametrize("shape", [(128, 256, 256), (100, 48, 256), (64, 1024, 256), (130, 16, 256), (1024, 1024, 256),
+@pytest.mark.parametrize("shape", [(128, 256, 256), (100, 48, 256), (64, 1024, 256), (130, 16, 256), (512, 1024, 256),
+                                   (768, 768, 256), (1024, 1024, 256),
                                    (100, 48, 512), (130, 16, 8192), (768, 1536, 256)])
 @pytest.mark.parametrize("with_bias", [True, False])
 def test_one_launch_equals_primitives_and_oracle(shape, with_bias):
@@ -76,12 +78,14 @@ def test_one_launch_equals_primitives_and_oracle(shape, with_bias):
     gemm_close(to_f64(a.y), fw["y"], bf16_out=True)
 
 
+@pytest.mark.parametrize("shape", [(128, 256, 256), (1024, 1024, 256)])
 @pytest.mark.parametrize("xs, ws", [(0.0, 1.0), (float("inf"), 2.0), (1.0, 1e30)])
-def test_one_launch_specials(xs, ws):
+def test_one_launch_specials(xs, ws, shape):
     """Infinities, NaNs and saturating values in x and W, a zero or infinite x scale, a weight
-    scale that saturates everything: every output equals the individual calls' (y included,
-    whatever it holds)."""
-    M, N, K = 128, 256, 256
+    scale that saturates everything (both one-launch kernels: 32 x 32 and 64 x 64 tiles): every
+    output equals the individual calls' (y included, whatever it holds)."""
+    M, N, K = shape
+    print(f"one-launch specials {shape} xs={xs} ws={ws}", flush=True)
     xh = S.normal_bf16(S.seed_for(9, 3), (M, K), 1.0)
     wh = S.normal_bf16(S.seed_for(9, 4), (N, K), 1.0)
     for (i, j, v) in [(0, 0, 0x7F80), (5, 200, 0xFF80), (127, 255, 0x7FC0), (64, 31, 0x7F7F)]:
@@ -104,11 +108,13 @@ def test_one_launch_specials(xs, ws):
     assert np.array_equal(u8_host(a.x8), q) and f32_bits(a.am[0].item()) == f32_bits(am)
 
 
-def test_one_launch_cached_weight_and_graph():
+@pytest.mark.parametrize("shape", [(128, 256, 256), (1024, 1024, 256)])
+def test_one_launch_cached_weight_and_graph(shape):
     """With the weight's flag at 1 the layer multiplies by the cached codes and inverse scale and
     writes nothing of W (a changed bfloat16 W is not seen); captured once and replayed with the
-    flag and x changing between replays, every replay equals the individual calls."""
-    M, N, K = 128, 256, 256
+    flag and x changing between replays, every replay equals the individual calls (both
+    one-launch kernels)."""
+    M, N, K = shape
     xh = [S.normal_bf16(S.seed_for(9, 10 + k), (M, K), 1.0) for k in range(3)]
     wh0 = S.normal_bf16(S.seed_for(9, 20), (N, K), 1.0)
     wh1 = S.normal_bf16(S.seed_for(9, 21), (N, K), 3.0)
@@ -148,11 +154,14 @@ def test_one_launch_cached_weight_and_graph():
         gemm_close(to_f64(a.y), fw["y"], bf16_out=True)
 
 
-@pytest.mark.parametrize("shape, one", [((128, 256, 256), True), ((1024, 1024, 256), True), ((128, 256, 512), False),
-                                        ((768, 1536, 256), False)])
+@pytest.mark.parametrize("shape, one", [((128, 256, 256), "k_linear_fwd_tiny"), ((512, 1024, 256), "k_linear_fwd_tiny"),
+                                        ((768, 768, 256), "k_linear_fwd_small"),
+                                        ((1024, 1024, 256), "k_linear_fwd_small"), ((128, 256, 512), None),
+                                        ((768, 1536, 256), None)])
 def test_dispatch_rule_launches(shape, one):
-    """Inside the rule the forward is the single k_linear_fwd_small launch; outside it the cast
-    launch and the GEMM launch (both give the same bits; this checks which one ran)."""
+    """Inside the rule the forward is a single launch: k_linear_fwd_tiny (32 x 32 tiles) up to
+    128 blocks of 64 x 64, k_linear_fwd_small beyond; outside it the cast launch and the GEMM
+    launch (all give the same bits; this checks which one ran)."""
     M, N, K = shape
     x = bf16_dev(S.normal_bf16(S.seed_for(9, 30), (M, K), 1.0))
     w = bf16_dev(S.normal_bf16(S.seed_for(9, 31), (N, K), 1.0))
@@ -165,6 +174,6 @@ def test_dispatch_rule_launches(shape, one):
     fp8 = [n for n in names if "fp8ds" in n]
     print(f"dispatch {shape}: {fp8}", flush=True)
     if one:
-        assert len(fp8) == 1 and "k_linear_fwd_small" in fp8[0]
+        assert len(fp8) == 1 and one in fp8[0]
     else:
-        assert not any("k_linear_fwd_small" in n for n in fp8) and len(fp8) == 2
+        assert not any("k_linear_fwd" in n for n in fp8) and len(fp8) == 2
