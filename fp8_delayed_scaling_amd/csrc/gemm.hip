@@ -1423,39 +1423,53 @@ __global__ __launch_bounds__(256) void k_linear_fwd_small(const SmallFwdArgs a) 
 __global__ __launch_bounds__(256) void k_linear_fwd_tiny(const SmallFwdArgs a) {
     __shared__ __align__(16) uint8_t sx[kTinyTile * kFam16K];
     __shared__ __align__(16) uint8_t sw[kTinyTile * kFam16K];
-    const int tm = blockIdx.x / a.tiles_n, tn = blockIdx.x - (blockIdx.x / a.tiles_n) * a.tiles_n;
+    const int tm = blockIdx.y, tn = blockIdx.x;   // a 2-D grid: no division by the tile count
     const int m0 = tm * kTinyTile, n0 = tn * kTinyTile;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int M = a.M, N = a.N;
-    const bool wcached = a.w_noop != nullptr && *a.w_noop == 1.0f;
-    const float xs = *a.x_scale;
-    const float ws = *a.w_scale;
-    const float sa = 1.0f / xs;
-    const float sb = wcached ? *a.w_scale_inv : 1.0f / ws;
-    if (blockIdx.x == 0 && t == 0) {
-        *a.x_scale_inv = sa;
-        if (!wcached) *a.w_scale_inv = sb;
-    }
-    const bool own_x = tn == 0, own_w = tm == 0 && !wcached;   // block-uniform
-    // ---- casts: thread t takes operand t / 128 (x, W), row (t / 4) % 32, K values 64 (t % 4) ..
+    // thread t casts operand t / 128 (x, W), row (t / 4) % 32, K values 64 (t % 4) ..
     const bool is_w = wave >= 2;                                // wave-uniform
     const int row = (t >> 2) & 31, q = t & 3;
     const int grow = (is_w ? n0 : m0) + row, lim = is_w ? N : M;
     const int64_t srow = min(grow, lim - 1);                    // rows past M / N repeat the last
+    // every load that needs no other value goes out first: the bias of this lane's four output
+    // columns and the bfloat16 rows (W's also when the weight turns out to be cached: unused then)
+    const int r16 = lane & 15, g = lane >> 4, wm = wave >> 1, wn = wave & 1;
+    const int xrow = m0 + wm * 16 + r16, col = n0 + wn * 16 + g * 4;
+    // (unconditional loads, so they issue together: without a bias they read x_scale's first bytes)
+    const bool has_bias = a.bias != nullptr;
+    const uint16_t *bsrc = has_bias ? a.bias : reinterpret_cast<const uint16_t *>(a.x_scale);
+    uint16_t braw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) braw[u] = bsrc[has_bias ? min(col + u, N - 1) : 0];
+    uint32_t v0[16], v1[16];
+    {
+        const uint16_t *src = (is_w ? a.w : a.x) + srow * kFam16K + q * 64;
+        load32_bf16(src, v0);
+        load32_bf16(src + 32, v1);
+    }
+    // the four scalars in one round (the flag read from x_scale when there is none; w_scale_inv
+    // is used only for a cached weight, which no block rewrites)
+    const float flag = *(a.w_noop != nullptr ? a.w_noop : a.x_scale);
+    const float xs = *a.x_scale, ws = *a.w_scale, wsi = *a.w_scale_inv;
+    const bool wcached = a.w_noop != nullptr && flag == 1.0f;
+    const float sa = 1.0f / xs;
+    const float sb = wcached ? wsi : 1.0f / ws;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && t == 0) {
+        *a.x_scale_inv = sa;
+        if (!wcached) *a.w_scale_inv = sb;
+    }
+    const bool own_x = tn == 0, own_w = tm == 0 && !wcached;   // block-uniform
     uint8_t *lds = is_w ? sw : sx;
     i32x8 c0, c1;
     uint32_t mag = 0;
     if (is_w && wcached) {
         const u32x4 *p = reinterpret_cast<const u32x4 *>(a.w8 + srow * kFam16K + q * 64);
-        const u32x4 v0 = p[0], v1 = p[1], v2 = p[2], v3 = p[3];
-        c0 = i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-        c1 = i32x8{(int)v2.x, (int)v2.y, (int)v2.z, (int)v2.w, (int)v3.x, (int)v3.y, (int)v3.z, (int)v3.w};
+        const u32x4 p0 = p[0], p1 = p[1], p2 = p[2], p3 = p[3];
+        c0 = i32x8{(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w, (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
+        c1 = i32x8{(int)p2.x, (int)p2.y, (int)p2.z, (int)p2.w, (int)p3.x, (int)p3.y, (int)p3.z, (int)p3.w};
     } else {
-        const uint16_t *src = (is_w ? a.w : a.x) + srow * kFam16K + q * 64;
-        uint32_t v0[16], v1[16];
-        load32_bf16(src, v0);
-        load32_bf16(src + 32, v1);
         const float s = is_w ? ws : xs;
         const bool plain = scale_is_plain(s);
         uint32_t t0, t1;
@@ -1477,17 +1491,14 @@ __global__ __launch_bounds__(256) void k_linear_fwd_tiny(const SmallFwdArgs a) {
         store32_codes(dst, c0);
         store32_codes(dst + 32, c1);
     }
-    if (own) {
+    float *amax_slot = is_w ? a.w_amax : a.x_amax;
+    if (own && amax_slot != nullptr) {
         const uint32_t m = wave_max_u32(mag);
-        if (lane == 0 && m != 0u) atomicMax(reinterpret_cast<unsigned int *>(is_w ? a.w_amax : a.x_amax), m << 16);
+        if (lane == 0 && m != 0u) atomicMax(reinterpret_cast<unsigned int *>(amax_slot), m << 16);
     }
-    // bias of this lane's four output columns, loaded while the casts finish
-    const int r16 = lane & 15, g = lane >> 4, wm = wave >> 1, wn = wave & 1;
-    const int xrow = m0 + wm * 16 + r16, col = n0 + wn * 16 + g * 4;
-    const bool has_bias = a.bias != nullptr;
     float bv[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) bv[u] = has_bias ? __uint_as_float((uint32_t)a.bias[min(col + u, N - 1)] << 16) : 0.f;
+    for (int u = 0; u < 4; ++u) bv[u] = has_bias ? __uint_as_float((uint32_t)braw[u] << 16) : 0.f;
     __syncthreads();
     // ---- w8_t rows k, columns n0 .. n0 + 31 from the W tile: thread t transposes the 4 x 8 byte
     // block k = 4 (t / 4) .., n = 8 (t % 4) ..
@@ -1672,8 +1683,8 @@ hipError_t launch_linear_fwd_small(const uint16_t *x, const uint16_t *w, const u
     const int64_t blocks64 = ((M + kSmallTile - 1) / kSmallTile) * ((N + kSmallTile - 1) / kSmallTile);
     if (blocks64 <= kTinyMaxBlocks64) {
         a.tiles_n = (int)((N + kTinyTile - 1) / kTinyTile);
-        const unsigned grid = (unsigned)(((M + kTinyTile - 1) / kTinyTile) * a.tiles_n);
-        k_linear_fwd_tiny<<<dim3(grid), dim3(256), 0, st>>>(a);
+        const dim3 grid((unsigned)a.tiles_n, (unsigned)((M + kTinyTile - 1) / kTinyTile));
+        k_linear_fwd_tiny<<<grid, dim3(256), 0, st>>>(a);
         return hipGetLastError();
     }
     a.tiles_n = (int)((N + kSmallTile - 1) / kSmallTile);

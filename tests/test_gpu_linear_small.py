@@ -109,6 +109,28 @@ def test_one_launch_specials(xs, ws, shape):
 
 
 @pytest.mark.parametrize("shape", [(128, 256, 256), (1024, 1024, 256)])
+def test_one_launch_without_amax_slots(shape):
+    """The amax slots are optional: without them (NULL) the one-launch forward writes the same
+    codes, inverse scales and y as with them."""
+    M, N, K = shape
+    print(f"one-launch forward without amax slots {shape}", flush=True)
+    x = bf16_dev(S.normal_bf16(S.seed_for(9, 40), (M, K), 1.0))
+    w = bf16_dev(S.normal_bf16(S.seed_for(9, 41), (N, K), 1.0))
+    b = bf16_dev(S.normal_bf16(S.seed_for(9, 42), (N,), 0.1))
+    scales = torch.tensor([2.0, 32.0], **F32)
+    a, r = Fwd(M, N, K), Fwd(M, N, K)
+    F.fp8_linear_fwd(x, w, b, scales[0:1], None, a.x8, None, a.sinv[0:1], scales[1:2], None, a.w8, a.w8t,
+                     a.sinv[1:2], None, a.y)
+    _layer_call(x, w, b, scales, r)
+    torch.cuda.synchronize()
+    for name in ("x8", "w8", "w8t"):
+        assert torch.equal(getattr(a, name), getattr(r, name)), name
+    assert torch.equal(a.sinv.view(torch.int32), r.sinv.view(torch.int32))
+    assert torch.equal(a.y.view(torch.int16), r.y.view(torch.int16))
+    assert not torch.any(a.am)    # untouched
+
+
+@pytest.mark.parametrize("shape", [(128, 256, 256), (1024, 1024, 256)])
 def test_one_launch_cached_weight_and_graph(shape):
     """With the weight's flag at 1 the layer multiplies by the cached codes and inverse scale and
     writes nothing of W (a changed bfloat16 W is not seen); captured once and replayed with the
