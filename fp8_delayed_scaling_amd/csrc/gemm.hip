@@ -1660,9 +1660,9 @@ hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64
 // N % 16 == 0 (whole 16-byte chunks of w8_t rows), and x's transpose not asked for.
 constexpr int64_t kSmallFwdMaxBlocks = 256;
 // Up to this many 64 x 64 blocks the 32 x 32 tiles of k_linear_fwd_tiny are faster (through the
-// C ABI, back to back: [128, 256, 256] 4.9 against 7.1 us, [512, 1024, 256] 6.1 against 7.2 us;
-// [768, 768, 256] even, [1024, 1024, 256] 9.2 against 7.4 us).
-constexpr int64_t kTinyMaxBlocks64 = 128;
+// C ABI, back to back: [128, 256, 256] 4.3 against 7.1 us, [768, 768, 256] 6.4 against 7.2 us,
+// [1024, 768, 256] 6.5 against 7.3 us; [1024, 1024, 256] 8.4 against 7.4 us).
+constexpr int64_t kTinyMaxBlocks64 = 192;
 constexpr int64_t kSmallFwdMaxTiles = 39;
 bool linear_fwd_small_ok(int64_t M, int64_t N, int64_t K, const uint8_t *x8_t) {
     if (x8_t != nullptr || M <= 0 || N <= 0 || K != kFam16K || N % 16 != 0) return false;

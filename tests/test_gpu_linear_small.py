@@ -1,6 +1,6 @@
 """The one-launch forward of small layers (fp8_linear_fwd when K == 256, N % 16 == 0, no x
 transpose, at most 256 output blocks of 64 x 64 and fewer than 40 of 256 x 256; 32 x 32 tiles up
-to 128 blocks of 64 x 64) against the
+to 192 blocks of 64 x 64) against the
 individual calls (cast of x, cast+transpose of W, GEMM + bias: every output bit for bit) and
 against the oracle (codes, amaxes and inverse scales exact, y within the GEMM tolerance),
 including the cached-weight flag, non-finite inputs, scales that are not plain, graph replay, and
@@ -53,7 +53,7 @@ def _equal(a, b):
 # the small layer [128, 256] x [256, 256], a ragged M, a narrow N, a wide N, the largest block
 # count (16 x 16 blocks of 64 x 64); then layers outside the rule: K = 512 and 8192, 288 blocks
 @pytest.mark.parametrize("shape", [(128, 256, 256), (100, 48, 256), (64, 1024, 256), (130, 16, 256), (512, 1024, 256),
-                                   (768, 768, 256), (1024, 1024, 256),
+                                   (1024, 768, 256), (1024, 832, 256), (1024, 1024, 256),
                                    (100, 48, 512), (130, 16, 8192), (768, 1536, 256)])
 @pytest.mark.parametrize("with_bias", [True, False])
 def test_one_launch_equals_primitives_and_oracle(shape, with_bias):
@@ -177,12 +177,12 @@ def test_one_launch_cached_weight_and_graph(shape):
 
 
 @pytest.mark.parametrize("shape, one", [((128, 256, 256), "k_linear_fwd_tiny"), ((512, 1024, 256), "k_linear_fwd_tiny"),
-                                        ((768, 768, 256), "k_linear_fwd_small"),
+                                        ((768, 768, 256), "k_linear_fwd_tiny"), ((1024, 832, 256), "k_linear_fwd_small"),
                                         ((1024, 1024, 256), "k_linear_fwd_small"), ((128, 256, 512), None),
                                         ((768, 1536, 256), None)])
 def test_dispatch_rule_launches(shape, one):
     """Inside the rule the forward is a single launch: k_linear_fwd_tiny (32 x 32 tiles) up to
-    128 blocks of 64 x 64, k_linear_fwd_small beyond; outside it the cast launch and the GEMM
+    192 blocks of 64 x 64, k_linear_fwd_small beyond; outside it the cast launch and the GEMM
     launch (all give the same bits; this checks which one ran)."""
     M, N, K = shape
     x = bf16_dev(S.normal_bf16(S.seed_for(9, 30), (M, K), 1.0))
