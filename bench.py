@@ -63,6 +63,8 @@ def parse():
     p.add_argument("--traffic-probe", action="store_true",
                    help="only launch one plain 1 GiB device copy and one forward GEMM (for rocprofv3 --pmc "
                         "FETCH_SIZE / WRITE_SIZE passes: the copy calibrates the counters)")
+    p.add_argument("--small-only", action="store_true",
+                   help="only the small-layer forward [128,256] x [256,256] (for a kernel trace)")
     p.add_argument("--casts-only", action="store_true",
                    help="only the cold cast-family timings (cast+transpose sweep, cast+amax, backward prep), "
                         "printed as one JSON line (for an isolated rocprofv3 kernel trace)")
@@ -153,6 +155,10 @@ def main():
 
     def bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.small_only:
+        print(json.dumps({"small_only": {"small_forward_128x256x256": small_forward(F, S, torch, np, dev, bf16)}}))
+        return
 
     if args.casts_only:
         res = cast_family(F, S, torch, np, dev, bf16)
@@ -456,30 +462,12 @@ def cast_family(F, S, torch, np, dev, bf16):
     return out
 
 
-def extras(F, S, torch, np, dev, bf16, step):
-    """Timings beyond the step.  The GEMM extras use the step's own FP8 operands (x8, W8, W8^T,
-    dy8 cast from the normal-distributed inputs at the step's scales): a GEMM's power draw, and
-    with it the clock it runs at, depends on the operands' bits."""
-    out = {}
-    u8 = dict(device=dev, dtype=torch.uint8)
+def small_forward(F, S, torch, np, dev, bf16):
+    """The small layer [128,256] x [256,256] (bias, E4M3, one launch): host time per call back to
+    back through the binding, a prepared call, the C ABI with its arguments marshalled once, a
+    torch graph replay and hipGraphLaunch of the same graph."""
     f32 = dict(device=dev, dtype=torch.float32)
-    flush = torch.empty(512 << 20, **u8)     # 512 MB: evicts the 256 MB MALL and the L2s
-
-    def cold_time(fn, reps=10):
-        ts = []
-        for _ in range(reps):
-            flush.zero_()
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
-            fn()
-            e.record()
-            torch.cuda.synchronize()
-            ts.append(s.elapsed_time(e))
-        return float(np.median(ts))
-
-    out.update(cast_family(F, S, torch, np, dev, bf16))
-
-    # small forward layer: eager call vs graph replay (one launch: the casts run inside the GEMM kernel)
+    u8 = dict(device=dev, dtype=torch.uint8)
     Ms, Ns, Ks = 128, 256, 256
     xs, wsm, bs = bf16(S.normal_bf16(S.seed_for(0, 0), (Ms, Ks), 1.0)), bf16(S.normal_bf16(S.seed_for(0, 1), (Ns, Ks), 1.0)), \
         bf16(S.normal_bf16(S.seed_for(0, 2), (Ns,), 0.1))
@@ -548,10 +536,35 @@ def extras(F, S, torch, np, dev, bf16, step):
             hip_graph_us = round((time.perf_counter() - t) / 200 * 1e6, 2)
     except (OSError, AttributeError, TypeError, ValueError, RuntimeError):
         pass
-    out["small_forward_128x256x256"] = {"eager_us_per_call": round(eager_us, 2), "graph_replay_us": round(graph_us, 2),
-                                        "c_abi_eager_us_per_call": round(raw_us, 2),
-                                        "prepared_us_per_call": round(prepared_us, 2),
-                                        "hip_graph_launch_us": hip_graph_us, "launches": 1}
+    return {"eager_us_per_call": round(eager_us, 2), "graph_replay_us": round(graph_us, 2),
+            "c_abi_eager_us_per_call": round(raw_us, 2), "prepared_us_per_call": round(prepared_us, 2),
+            "hip_graph_launch_us": hip_graph_us, "launches": 1}
+
+
+def extras(F, S, torch, np, dev, bf16, step):
+    """Timings beyond the step.  The GEMM extras use the step's own FP8 operands (x8, W8, W8^T,
+    dy8 cast from the normal-distributed inputs at the step's scales): a GEMM's power draw, and
+    with it the clock it runs at, depends on the operands' bits."""
+    out = {}
+    u8 = dict(device=dev, dtype=torch.uint8)
+    f32 = dict(device=dev, dtype=torch.float32)
+    flush = torch.empty(512 << 20, **u8)     # 512 MB: evicts the 256 MB MALL and the L2s
+
+    def cold_time(fn, reps=10):
+        ts = []
+        for _ in range(reps):
+            flush.zero_()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            ts.append(s.elapsed_time(e))
+        return float(np.median(ts))
+
+    out.update(cast_family(F, S, torch, np, dev, bf16))
+
+    out["small_forward_128x256x256"] = small_forward(F, S, torch, np, dev, bf16)
 
     # N-chunked GEMM + bias, M=8192, K=N=12288 (x8 and the first 12288 rows of W8), one stream
     # per chunk, captured as one graph
