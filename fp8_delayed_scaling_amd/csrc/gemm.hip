@@ -44,8 +44,8 @@
 // k_gemm_bias (any K % 16 == 0): global -> registers -> LDS with double-buffered 128-byte K
 // slices, the K tail zero-filled.
 //
-// k_linear_fwd_small / k_linear_fwd_tiny (further down): the whole forward of a small layer
-// (casts of x and W, GEMM + bias) in one launch, with the MFMAs of k_gemm_small16.
+// k_linear_fwd_small (further down): the whole forward of a small layer (casts of x and W, GEMM +
+// bias) in one launch, with the MFMAs of k_gemm_small16.
 #include <type_traits>
 
 #include "device_common.h"
@@ -1211,20 +1211,24 @@ __global__ __launch_bounds__(64) void k_gemm_small16(const uint8_t *__restrict__
 }
 
 // ------------------------------------------------------------------------------------------
-// k_linear_fwd_small: the forward of a small FP8 linear layer in one launch.  At the size of a
-// [128, 256] x [256, 256] layer both kernels of the two-launch form are pure latency (a cast
-// launch of two tiles, then eight waves of GEMM), so here each 64 x 64 output tile's block casts
-// the bfloat16 rows it multiplies itself: per 128-byte K step, wave w casts x rows 16 w .. and W
-// rows 16 w .. of the tile in registers (the x fragment feeds its own MFMAs; the W fragments are
-// exchanged through a 64 x 128-byte LDS tile), and the MFMAs run in the K order of
-// k_gemm_small16 on the same fragments, so y is identical.  The casts' outputs are written by
-// the blocks that own them: tile column 0 writes x8 and folds x's amax; tile row 0 writes w8,
-// folds W's amax and writes w8_t from the LDS tile.  A cached weight (*w_noop == 1) is read as
-// codes from w8 and nothing of W is written.  Every code equals the cast kernels' (same clamp +
-// hardware conversion, the exact encoder for a fragment holding an inf / NaN or under a zero /
-// non-finite scale), and 1/scale is formed as the cast kernels form it.
+// k_linear_fwd_small<TILE>: the forward of a small FP8 linear layer in one launch.  At the size
+// of a [128, 256] x [256, 256] layer both kernels of the two-launch form are pure latency (a cast
+// launch of two tiles, then eight waves of GEMM), so here each TILE x TILE output tile's block
+// (TILE 32 or 64, 8 TILE threads) casts the bfloat16 rows it multiplies itself.  K is 256, so a
+// block casts every row it needs in one pass: the first 4 TILE threads the tile's x rows, the
+// others its W rows, each thread 64 consecutive K values (four per row); the codes go to two
+// TILE x 256-byte LDS tiles (16-byte chunk c of row r at chunk c ^ (r % 16)).  After one barrier
+// each wave multiplies TILE / 32 of the 16 x 16 output tiles (one x slice, TILE / 32 adjacent W
+// slices) with the two 128-byte K steps of k_gemm_small16 in its order, on the same fragments,
+// so y is identical.  The casts' outputs are written by the blocks that own them: tile column 0
+// writes x8 and folds x's amax; tile row 0 writes w8, folds W's amax and writes w8_t from the W
+// tile with 4 x 4 byte register transposes.  A cached weight (*w_noop == 1) is read as codes
+// from w8 and nothing of W is written.  Every code equals the cast kernels' (same clamp +
+// hardware conversion, the exact encoder for a group holding an inf / NaN or under a zero /
+// non-finite scale), and 1/scale is formed as the cast kernels form it.  Every load that depends
+// on nothing else (bias, bfloat16 rows, the four scalars) is issued first and without branches;
+// each wave folds its amax with one atomic (no read first: a few hundred blocks at most).
 // ------------------------------------------------------------------------------------------
-constexpr int kTinyTile = 32;
 struct SmallFwdArgs {
     const uint16_t *x, *w, *bias;
     const float *x_scale, *w_scale, *w_noop;
@@ -1272,177 +1276,38 @@ __device__ __forceinline__ void store32_codes(uint8_t *p, const i32x8 &c) {
     reinterpret_cast<u32x4 *>(p)[1] = u32x4{(uint32_t)c[4], (uint32_t)c[5], (uint32_t)c[6], (uint32_t)c[7]};
 }
 
-__global__ __launch_bounds__(256) void k_linear_fwd_small(const SmallFwdArgs a) {
-    __shared__ __align__(16) uint8_t sw[kSmallTile * kQK];   // the tile's W codes of one K step: [row][k]
-    const int tm = blockIdx.x / a.tiles_n, tn = blockIdx.x - (blockIdx.x / a.tiles_n) * a.tiles_n;
-    const int m0 = tm * kSmallTile, n0 = tn * kSmallTile;
-    const int t = threadIdx.x, lane = t & 63, r16 = lane & 15, g = lane >> 4;
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // 16-row slice of x and of W
-    const int M = a.M, N = a.N, K = a.K;
-    const float xs = *a.x_scale;
-    const bool wcached = a.w_noop != nullptr && *a.w_noop == 1.0f;
-    const float ws = *a.w_scale;
-    const float sa = 1.0f / xs;
-    const float sb = wcached ? *a.w_scale_inv : 1.0f / ws;
-    if (blockIdx.x == 0 && t == 0) {
-        *a.x_scale_inv = sa;
-        if (!wcached) *a.w_scale_inv = sb;
-    }
-    const bool own_x = tn == 0, own_w = tm == 0 && !wcached;   // block-uniform
-    const bool plain_x = scale_is_plain(xs), plain_w = scale_is_plain(ws);
-    // lane l of wave w supplies row 16 w + l % 16 of the x and W tiles and K bytes
-    // [32 (l / 16), +32) of each 128-byte step; rows past M / N repeat the last row (never stored)
-    const int xrow = m0 + wave * 16 + r16, wrow = n0 + wave * 16 + r16;
-    const uint16_t *xsrc = a.x + (int64_t)min(xrow, M - 1) * K + g * 32;
-    const uint16_t *wsrc = a.w + (int64_t)min(wrow, N - 1) * K + g * 32;
-    const uint8_t *w8src = a.w8 + (int64_t)min(wrow, N - 1) * K + g * 32;
-    f32x4 acc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bool has_bias = a.bias != nullptr;
-    const uint16_t *bsrc = has_bias ? a.bias : reinterpret_cast<const uint16_t *>(a.x_scale);
-    uint32_t braw[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) braw[j][u] = bsrc[has_bias ? min(n0 + j * 16 + g * 4 + u, N - 1) : 0];
-    uint32_t xam = 0, wam = 0;
-    const int nk = K / kQK;
-    // the next step's rows are loaded before this step is cast (one step ahead)
-    uint32_t nx[16], nw[16] = {};
-    load32_bf16(xsrc, nx);
-    if (wcached) {
-        const u32x4 *q = reinterpret_cast<const u32x4 *>(w8src);
-        const u32x4 lo = q[0], hi = q[1];
-        nw[0] = lo.x; nw[1] = lo.y; nw[2] = lo.z; nw[3] = lo.w; nw[4] = hi.x; nw[5] = hi.y; nw[6] = hi.z; nw[7] = hi.w;
-    } else {
-        load32_bf16(wsrc, nw);
-    }
-    for (int kt = 0; kt < nk; ++kt) {
-        const int kc = kt * kQK;
-        uint32_t vx[16], vw[16];
-#pragma unroll
-        for (int q = 0; q < 16; ++q) { vx[q] = nx[q]; vw[q] = nw[q]; }
-        if (kt + 1 < nk) {
-            load32_bf16(xsrc + kc + kQK, nx);
-            if (wcached) {
-                const u32x4 *q = reinterpret_cast<const u32x4 *>(w8src + kc + kQK);
-                const u32x4 lo = q[0], hi = q[1];
-                nw[0] = lo.x; nw[1] = lo.y; nw[2] = lo.z; nw[3] = lo.w; nw[4] = hi.x; nw[5] = hi.y; nw[6] = hi.z; nw[7] = hi.w;
-            } else {
-                load32_bf16(wsrc + kc + kQK, nw);
-            }
-        }
-        i32x8 fbw;
-        if (wcached)
-            fbw = i32x8{(int)vw[0], (int)vw[1], (int)vw[2], (int)vw[3], (int)vw[4], (int)vw[5], (int)vw[6], (int)vw[7]};
-        uint32_t tam;
-        const i32x8 fa = cast32_e4m3(vx, xs, plain_x, &tam);
-        if (own_x) {
-            xam = amax_pk(xam, tam);
-            if (xrow < M) store32_codes(a.x8 + (int64_t)xrow * K + kc + g * 32, fa);
-        }
-        if (!wcached) {
-            fbw = cast32_e4m3(vw, ws, plain_w, &tam);
-            if (own_w) {
-                wam = amax_pk(wam, tam);
-                if (wrow < N) store32_codes(a.w8 + (int64_t)wrow * K + kc + g * 32, fbw);
-            }
-        }
-        if (kt > 0) __syncthreads();   // every wave has read the previous step's W codes
-        store32_codes(sw + (wave * 16 + r16) * kQK + g * 32, fbw);
-        __syncthreads();
-        if (own_w) {
-            // w8_t rows kc + k, columns n0 .. n0 + 63 = sw[.][k]: thread t gathers k = t / 2,
-            // columns 32 (t % 2) .. + 31
-            const int k = t >> 1, c0 = (t & 1) * 32;
-            uint32_t d[8];
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-                d[c] = (uint32_t)sw[(c0 + 4 * c) * kQK + k] | ((uint32_t)sw[(c0 + 4 * c + 1) * kQK + k] << 8) |
-                       ((uint32_t)sw[(c0 + 4 * c + 2) * kQK + k] << 16) | ((uint32_t)sw[(c0 + 4 * c + 3) * kQK + k] << 24);
-            uint8_t *dst = a.w8_t + (int64_t)(kc + k) * N + n0 + c0;
-            if (n0 + c0 < N) reinterpret_cast<u32x4 *>(dst)[0] = u32x4{d[0], d[1], d[2], d[3]};
-            if (n0 + c0 + 16 < N) reinterpret_cast<u32x4 *>(dst)[1] = u32x4{d[4], d[5], d[6], d[7]};
-        }
-        i32x8 fb[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const u32x4 *q = reinterpret_cast<const u32x4 *>(sw + (j * 16 + r16) * kQK + g * 32);
-            const u32x4 lo = q[0], hi = q[1];
-            fb[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], fa, acc[j], kE4M3, kE4M3, 0, 0, 0, 0);
-    }
-    // epilogue as k_gemm_small16 (bfloat16 out): lane l of wave w holds y[m0 + 16 w + l % 16]
-    // [n0 + 16 j + 4 (l / 16) + u] in element u of acc[j]
-    // (N % 16 == 0: a lane's four columns are all inside or all outside; one 8-byte store each
-    // when y is 8-byte aligned)
-    const bool y8 = (reinterpret_cast<uintptr_t>(a.y) & 7u) == 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int col = n0 + j * 16 + g * 4;
-        float val[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float b = has_bias ? __uint_as_float(braw[j][u] << 16) : 0.f;
-            val[u] = dequant_bias(acc[j][u], sa, sb, b);
-        }
-        if (xrow < M && col < N) {
-            uint16_t *dst = a.y + (int64_t)xrow * N + col;
-            if (y8) {
-                *reinterpret_cast<u32x2 *>(dst) = u32x2{f32x2_to_bf16x2_rne(val[0], val[1]), f32x2_to_bf16x2_rne(val[2], val[3])};
-            } else {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) dst[u] = f32_to_bf16_rne(val[u]);
-            }
-        }
-    }
-    if (own_x) {
-        const uint32_t m = wave_max_u32(amax_unpack(xam));
-        if (lane == 0) fold_amax(a.x_amax, m);
-    }
-    if (own_w) {
-        const uint32_t m = wave_max_u32(amax_unpack(wam));
-        if (lane == 0) fold_amax(a.w_amax, m);
-    }
-}
-
-// k_linear_fwd_tiny: the same forward with 32 x 32 output tiles, for the smallest layers (four
-// times the blocks of the 64 x 64 form, so the casts spread over more CUs, and no barrier
-// between K steps).  K is 256, so a
-// block casts every row it needs in one pass: threads 0-127 the tile's 32 x rows, threads
-// 128-255 its 32 W rows, each thread 64 consecutive K values (four per row); the codes go to two
-// 32 x 256-byte LDS tiles (16-byte chunk c of row r at chunk c ^ (r % 16)), the owners' codes to
-// x8 / w8; after one barrier wave w multiplies x rows 16 (w / 2) .. by W rows 16 (w % 2) .. with
-// the two 128-byte K steps of k_gemm_small16 in its order (identical y), and the blocks of tile
-// row 0 write w8_t from the W tile with 4 x 4 byte register transposes.  Each wave folds its
-// amax with one atomic (no read first: at most a few dozen blocks fold).
-__global__ __launch_bounds__(256) void k_linear_fwd_tiny(const SmallFwdArgs a) {
-    __shared__ __align__(16) uint8_t sx[kTinyTile * kFam16K];
-    __shared__ __align__(16) uint8_t sw[kTinyTile * kFam16K];
+template <int TILE>
+__global__ __launch_bounds__(8 * TILE) void k_linear_fwd_small(const SmallFwdArgs a) {
+    constexpr int kRowsT = 4 * TILE;                  // threads casting one operand (four per row)
+    constexpr int kT16 = TILE / 16;                   // 16 x 16 output tiles per tile edge
+    constexpr int kPerWave = TILE / 32;               // 16 x 16 output tiles per wave
+    __shared__ __align__(16) uint8_t sx[TILE * kFam16K];
+    __shared__ __align__(16) uint8_t sw[TILE * kFam16K];
     const int tm = blockIdx.y, tn = blockIdx.x;   // a 2-D grid: no division by the tile count
-    const int m0 = tm * kTinyTile, n0 = tn * kTinyTile;
+    const int m0 = tm * TILE, n0 = tn * TILE;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int M = a.M, N = a.N;
-    // thread t casts operand t / 128 (x, W), row (t / 4) % 32, K values 64 (t % 4) ..
-    const bool is_w = wave >= 2;                                // wave-uniform
-    const int row = (t >> 2) & 31, q = t & 3;
+    // thread t casts operand t / (4 TILE) (x, W), row (t / 4) % TILE, K values 64 (t % 4) ..
+    const bool is_w = t >= kRowsT;                              // wave-uniform
+    const int row = (t >> 2) & (TILE - 1), q = t & 3;
     const int grow = (is_w ? n0 : m0) + row, lim = is_w ? N : M;
     const int64_t srow = min(grow, lim - 1);                    // rows past M / N repeat the last
-    // every load that needs no other value goes out first: the bias of this lane's four output
+    // every load that depends on nothing else goes out first: the bias of this lane's output
     // columns and the bfloat16 rows (W's also when the weight turns out to be cached: unused then)
-    const int r16 = lane & 15, g = lane >> 4, wm = wave >> 1, wn = wave & 1;
-    const int xrow = m0 + wm * 16 + r16, col = n0 + wn * 16 + g * 4;
     // (unconditional loads, so they issue together: without a bias they read x_scale's first bytes)
+    const int r16 = lane & 15, g = lane >> 4;
+    const int t0 = wave * kPerWave;                             // this wave's first output tile
+    const int tm16 = t0 / kT16, tn16 = t0 % kT16;               // its tiles: (tm16, tn16 + j)
+    const int xrow = m0 + tm16 * 16 + r16;
     const bool has_bias = a.bias != nullptr;
     const uint16_t *bsrc = has_bias ? a.bias : reinterpret_cast<const uint16_t *>(a.x_scale);
-    uint16_t braw[4];
+    uint16_t braw[kPerWave][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) braw[u] = bsrc[has_bias ? min(col + u, N - 1) : 0];
+    for (int j = 0; j < kPerWave; ++j)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            braw[j][u] = bsrc[has_bias ? min(n0 + (tn16 + j) * 16 + g * 4 + u, N - 1) : 0];
     uint32_t v0[16], v1[16];
     {
         const uint16_t *src = (is_w ? a.w : a.x) + srow * kFam16K + q * 64;
@@ -1472,10 +1337,10 @@ __global__ __launch_bounds__(256) void k_linear_fwd_tiny(const SmallFwdArgs a) {
     } else {
         const float s = is_w ? ws : xs;
         const bool plain = scale_is_plain(s);
-        uint32_t t0, t1;
-        c0 = cast32_e4m3(v0, s, plain, &t0);
-        c1 = cast32_e4m3(v1, s, plain, &t1);
-        mag = amax_unpack(amax_pk(t0, t1));
+        uint32_t m0b, m1b;
+        c0 = cast32_e4m3(v0, s, plain, &m0b);
+        c1 = cast32_e4m3(v1, s, plain, &m1b);
+        mag = amax_unpack(amax_pk(m0b, m1b));
     }
     {
         const int sw4 = row & 15;
@@ -1496,14 +1361,11 @@ __global__ __launch_bounds__(256) void k_linear_fwd_tiny(const SmallFwdArgs a) {
         const uint32_t m = wave_max_u32(mag);
         if (lane == 0 && m != 0u) atomicMax(reinterpret_cast<unsigned int *>(amax_slot), m << 16);
     }
-    float bv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) bv[u] = has_bias ? __uint_as_float((uint32_t)braw[u] << 16) : 0.f;
     __syncthreads();
-    // ---- w8_t rows k, columns n0 .. n0 + 31 from the W tile: thread t transposes the 4 x 8 byte
-    // block k = 4 (t / 4) .., n = 8 (t % 4) ..
+    // ---- w8_t rows k, columns n0 .. n0 + TILE - 1 from the W tile: thread t transposes the
+    // 4 x 8 byte block k = 4 (t / (TILE / 8)) .., n = 8 (t % (TILE / 8)) ..
     if (own_w) {
-        const int n8 = (t & 3) * 8, k4 = (t >> 2) * 4;
+        const int n8 = (t % (TILE / 8)) * 8, k4 = (t / (TILE / 8)) * 4;
         uint32_t d[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -1519,33 +1381,45 @@ __global__ __launch_bounds__(256) void k_linear_fwd_tiny(const SmallFwdArgs a) {
                 *reinterpret_cast<u32x2 *>(a.w8_t + (int64_t)(k4 + j) * N + n0 + n8) = u32x2{o[j], p[j]};
         }
     }
-    // ---- the two K steps: lane l supplies row l % 16 of its 16-row x and W slices and K bytes
+    // ---- the two K steps: lane l supplies row l % 16 of the 16-row x and W slices and K bytes
     // [32 (l / 16), +32) of each step
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[kPerWave];
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
         const int ch = 8 * st + 2 * g;
-        const int ra = wm * 16 + r16, rb = wn * 16 + r16;
+        const int ra = tm16 * 16 + r16;
         const u32x4 a0 = *reinterpret_cast<const u32x4 *>(sx + ra * kFam16K + ((ch ^ r16) << 4));
         const u32x4 a1 = *reinterpret_cast<const u32x4 *>(sx + ra * kFam16K + (((ch + 1) ^ r16) << 4));
-        const u32x4 b0 = *reinterpret_cast<const u32x4 *>(sw + rb * kFam16K + ((ch ^ r16) << 4));
-        const u32x4 b1 = *reinterpret_cast<const u32x4 *>(sw + rb * kFam16K + (((ch + 1) ^ r16) << 4));
         const i32x8 fa = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        const i32x8 fb = i32x8{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa, acc, kE4M3, kE4M3, 0, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < kPerWave; ++j) {
+            const int rb = (tn16 + j) * 16 + r16;
+            const u32x4 b0 = *reinterpret_cast<const u32x4 *>(sw + rb * kFam16K + ((ch ^ r16) << 4));
+            const u32x4 b1 = *reinterpret_cast<const u32x4 *>(sw + rb * kFam16K + (((ch + 1) ^ r16) << 4));
+            const i32x8 fb = i32x8{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+            acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa, acc[j], kE4M3, kE4M3, 0, 0, 0, 0);
+        }
     }
-    // ---- y: lane l holds y[xrow][col + u] in element u (N % 16 == 0: the four columns are all
-    // inside or all outside)
-    if (xrow < M && col < N) {
-        float val[4];
+    // ---- y: lane l holds y[xrow][col + u] of tile j in element u (N % 16 == 0: the four
+    // columns are all inside or all outside)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) val[u] = dequant_bias(acc[u], sa, sb, bv[u]);
-        uint16_t *dst = a.y + (int64_t)xrow * N + col;
-        if ((reinterpret_cast<uintptr_t>(a.y) & 7u) == 0) {
-            *reinterpret_cast<u32x2 *>(dst) = u32x2{f32x2_to_bf16x2_rne(val[0], val[1]), f32x2_to_bf16x2_rne(val[2], val[3])};
-        } else {
+    for (int j = 0; j < kPerWave; ++j) {
+        const int col = n0 + (tn16 + j) * 16 + g * 4;
+        if (xrow < M && col < N) {
+            float val[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) dst[u] = f32_to_bf16_rne(val[u]);
+            for (int u = 0; u < 4; ++u)
+                val[u] = dequant_bias(acc[j][u], sa, sb, has_bias ? __uint_as_float((uint32_t)braw[j][u] << 16) : 0.f);
+            uint16_t *dst = a.y + (int64_t)xrow * N + col;
+            if ((reinterpret_cast<uintptr_t>(a.y) & 7u) == 0) {
+                *reinterpret_cast<u32x2 *>(dst) =
+                    u32x2{f32x2_to_bf16x2_rne(val[0], val[1]), f32x2_to_bf16x2_rne(val[2], val[3])};
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) dst[u] = f32_to_bf16_rne(val[u]);
+            }
         }
     }
 }
@@ -1651,18 +1525,17 @@ hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64
     return hipGetLastError();
 }
 
-// The one-launch small forward applies where it beats the cast-pair launch + GEMM launch: K ==
-// 256 (two 128-byte steps; each further step adds about 1.9 us of casts, code stores, barriers
-// and transpose gathers, which loading the rows two steps ahead does not shorten: measured
-// through the C ABI, 10.8 against 9.6 us at [128, 256, 512], 35 against 16 us at K = 2048), at most 256 blocks of 64 x 64 (one per CU: 7.7 against 8.5 us
-// at [1024, 1024, 256], 10.2 against 9.6 us at [768, 1536, 256]), fewer than 40 tiles of
-// 256 x 256 (the GEMM of the two-launch form is then k_gemm_small16, whose bits it reproduces),
-// N % 16 == 0 (whole 16-byte chunks of w8_t rows), and x's transpose not asked for.
+// The one-launch small forward takes K == 256 (a block casts a row's 256 values in one pass), no
+// x transpose, N % 16 == 0 (whole 8-byte groups of w8_t rows), at most 256 blocks of 64 x 64 and
+// fewer than 40 tiles of 256 x 256 (the GEMM of the two-launch form is then k_gemm_small16, whose
+// bits it reproduces).  Measured through the C ABI, back to back, against the cast-pair launch +
+// GEMM launch: [1024, 1024, 256] 6.2 against 8.5 us; beyond 256 blocks the two are close
+// ([768, 1536, 256] 9.1 against 9.4 us) and then the two launches win ([1024, 2048, 256] 10.1
+// against 9.7 us).  Up to 128 blocks of 64 x 64 the 32 x 32 tiles are faster ([128, 256, 256]
+// 4.2 against 5.7 us, [512, 1024, 256] 5.3 against 6.0 us), beyond it the 64 x 64 tiles
+// ([768, 768, 256] 6.0 against 6.4 us, [1024, 1024, 256] 6.2 against 8.3 us).
 constexpr int64_t kSmallFwdMaxBlocks = 256;
-// Up to this many 64 x 64 blocks the 32 x 32 tiles of k_linear_fwd_tiny are faster (through the
-// C ABI, back to back: [128, 256, 256] 4.3 against 7.1 us, [768, 768, 256] 6.4 against 7.2 us,
-// [1024, 768, 256] 6.5 against 7.3 us; [1024, 1024, 256] 8.4 against 7.4 us).
-constexpr int64_t kTinyMaxBlocks64 = 192;
+constexpr int64_t kTinyMaxBlocks64 = 128;
 constexpr int64_t kSmallFwdMaxTiles = 39;
 bool linear_fwd_small_ok(int64_t M, int64_t N, int64_t K, const uint8_t *x8_t) {
     if (x8_t != nullptr || M <= 0 || N <= 0 || K != kFam16K || N % 16 != 0) return false;
@@ -1682,14 +1555,14 @@ hipError_t launch_linear_fwd_small(const uint16_t *x, const uint16_t *w, const u
     a.M = (int)M; a.N = (int)N; a.K = (int)K;
     const int64_t blocks64 = ((M + kSmallTile - 1) / kSmallTile) * ((N + kSmallTile - 1) / kSmallTile);
     if (blocks64 <= kTinyMaxBlocks64) {
-        a.tiles_n = (int)((N + kTinyTile - 1) / kTinyTile);
-        const dim3 grid((unsigned)a.tiles_n, (unsigned)((M + kTinyTile - 1) / kTinyTile));
-        k_linear_fwd_tiny<<<grid, dim3(256), 0, st>>>(a);
-        return hipGetLastError();
+        a.tiles_n = (int)((N + 31) / 32);
+        const dim3 grid((unsigned)a.tiles_n, (unsigned)((M + 31) / 32));
+        k_linear_fwd_small<32><<<grid, dim3(256), 0, st>>>(a);
+    } else {
+        a.tiles_n = (int)((N + 63) / 64);
+        const dim3 grid((unsigned)a.tiles_n, (unsigned)((M + 63) / 64));
+        k_linear_fwd_small<64><<<grid, dim3(512), 0, st>>>(a);
     }
-    a.tiles_n = (int)((N + kSmallTile - 1) / kSmallTile);
-    const unsigned grid = (unsigned)blocks64;
-    k_linear_fwd_small<<<dim3(grid), dim3(256), 0, st>>>(a);
     return hipGetLastError();
 }
 

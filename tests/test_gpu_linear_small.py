@@ -1,6 +1,6 @@
 """The one-launch forward of small layers (fp8_linear_fwd when K == 256, N % 16 == 0, no x
 transpose, at most 256 output blocks of 64 x 64 and fewer than 40 of 256 x 256; 32 x 32 tiles up
-to 192 blocks of 64 x 64) against the
+to 128 blocks of 64 x 64) against the
 individual calls (cast of x, cast+transpose of W, GEMM + bias: every output bit for bit) and
 against the oracle (codes, amaxes and inverse scales exact, y within the GEMM tolerance),
 including the cached-weight flag, non-finite inputs, scales that are not plain, graph replay, and
@@ -82,7 +82,7 @@ def test_one_launch_equals_primitives_and_oracle(shape, with_bias):
 @pytest.mark.parametrize("xs, ws", [(0.0, 1.0), (float("inf"), 2.0), (1.0, 1e30)])
 def test_one_launch_specials(xs, ws, shape):
     """Infinities, NaNs and saturating values in x and W, a zero or infinite x scale, a weight
-    scale that saturates everything (both one-launch kernels: 32 x 32 and 64 x 64 tiles): every
+    scale that saturates everything (both tile sizes of the one-launch kernel): every
     output equals the individual calls' (y included, whatever it holds)."""
     M, N, K = shape
     print(f"one-launch specials {shape} xs={xs} ws={ws}", flush=True)
@@ -134,8 +134,8 @@ def test_one_launch_without_amax_slots(shape):
 def test_one_launch_cached_weight_and_graph(shape):
     """With the weight's flag at 1 the layer multiplies by the cached codes and inverse scale and
     writes nothing of W (a changed bfloat16 W is not seen); captured once and replayed with the
-    flag and x changing between replays, every replay equals the individual calls (both
-    one-launch kernels)."""
+    flag and x changing between replays, every replay equals the individual calls (both tile
+    sizes of the one-launch kernel)."""
     M, N, K = shape
     xh = [S.normal_bf16(S.seed_for(9, 10 + k), (M, K), 1.0) for k in range(3)]
     wh0 = S.normal_bf16(S.seed_for(9, 20), (N, K), 1.0)
@@ -176,13 +176,14 @@ def test_one_launch_cached_weight_and_graph(shape):
         gemm_close(to_f64(a.y), fw["y"], bf16_out=True)
 
 
-@pytest.mark.parametrize("shape, one", [((128, 256, 256), "k_linear_fwd_tiny"), ((512, 1024, 256), "k_linear_fwd_tiny"),
-                                        ((768, 768, 256), "k_linear_fwd_tiny"), ((1024, 832, 256), "k_linear_fwd_small"),
-                                        ((1024, 1024, 256), "k_linear_fwd_small"), ((128, 256, 512), None),
+@pytest.mark.parametrize("shape, one", [((128, 256, 256), "k_linear_fwd_small<32>"),
+                                        ((512, 1024, 256), "k_linear_fwd_small<32>"),
+                                        ((768, 768, 256), "k_linear_fwd_small<64>"),
+                                        ((1024, 1024, 256), "k_linear_fwd_small<64>"), ((128, 256, 512), None),
                                         ((768, 1536, 256), None)])
 def test_dispatch_rule_launches(shape, one):
-    """Inside the rule the forward is a single launch: k_linear_fwd_tiny (32 x 32 tiles) up to
-    192 blocks of 64 x 64, k_linear_fwd_small beyond; outside it the cast launch and the GEMM
+    """Inside the rule the forward is a single launch: k_linear_fwd_small<32> (32 x 32 tiles) up
+    to 128 blocks of 64 x 64, k_linear_fwd_small<64> beyond; outside it the cast launch and the GEMM
     launch (all give the same bits; this checks which one ran)."""
     M, N, K = shape
     x = bf16_dev(S.normal_bf16(S.seed_for(9, 30), (M, K), 1.0))
