@@ -1276,19 +1276,21 @@ __device__ __forceinline__ void store32_codes(uint8_t *p, const i32x8 &c) {
     reinterpret_cast<u32x4 *>(p)[1] = u32x4{(uint32_t)c[4], (uint32_t)c[5], (uint32_t)c[6], (uint32_t)c[7]};
 }
 
-template <int TILE>
+template <int TILE, int KK>
 __global__ __launch_bounds__(8 * TILE) void k_linear_fwd_small(const SmallFwdArgs a) {
     constexpr int kRowsT = 4 * TILE;                  // threads casting one operand (four per row)
     constexpr int kT16 = TILE / 16;                   // 16 x 16 output tiles per tile edge
     constexpr int kPerWave = TILE / 32;               // 16 x 16 output tiles per wave
-    __shared__ __align__(16) uint8_t sx[TILE * kFam16K];
-    __shared__ __align__(16) uint8_t sw[TILE * kFam16K];
+    constexpr int kVpt = KK / 4;                      // K values (code bytes) per casting thread
+    constexpr int kG = kVpt / 32;                     // groups of 32 values per thread
+    __shared__ __align__(16) uint8_t sx[TILE * KK];
+    __shared__ __align__(16) uint8_t sw[TILE * KK];
     const int tm = blockIdx.y, tn = blockIdx.x;   // a 2-D grid: no division by the tile count
     const int m0 = tm * TILE, n0 = tn * TILE;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int M = a.M, N = a.N;
-    // thread t casts operand t / (4 TILE) (x, W), row (t / 4) % TILE, K values 64 (t % 4) ..
+    // thread t casts operand t / (4 TILE) (x, W), row (t / 4) % TILE, K values kVpt (t % 4) ..
     const bool is_w = t >= kRowsT;                              // wave-uniform
     const int row = (t >> 2) & (TILE - 1), q = t & 3;
     const int grow = (is_w ? n0 : m0) + row, lim = is_w ? N : M;
@@ -1308,11 +1310,11 @@ __global__ __launch_bounds__(8 * TILE) void k_linear_fwd_small(const SmallFwdArg
 #pragma unroll
         for (int u = 0; u < 4; ++u)
             braw[j][u] = bsrc[has_bias ? min(n0 + (tn16 + j) * 16 + g * 4 + u, N - 1) : 0];
-    uint32_t v0[16], v1[16];
+    uint32_t v[kG][16];
     {
-        const uint16_t *src = (is_w ? a.w : a.x) + srow * kFam16K + q * 64;
-        load32_bf16(src, v0);
-        load32_bf16(src + 32, v1);
+        const uint16_t *src = (is_w ? a.w : a.x) + srow * KK + q * kVpt;
+#pragma unroll
+        for (int c = 0; c < kG; ++c) load32_bf16(src + 32 * c, v[c]);
     }
     // the four scalars in one round (the flag read from x_scale when there is none; w_scale_inv
     // is used only for a cached weight, which no block rewrites)
@@ -1327,34 +1329,43 @@ __global__ __launch_bounds__(8 * TILE) void k_linear_fwd_small(const SmallFwdArg
     }
     const bool own_x = tn == 0, own_w = tm == 0 && !wcached;   // block-uniform
     uint8_t *lds = is_w ? sw : sx;
-    i32x8 c0, c1;
+    i32x8 cd[kG];
     uint32_t mag = 0;
     if (is_w && wcached) {
-        const u32x4 *p = reinterpret_cast<const u32x4 *>(a.w8 + srow * kFam16K + q * 64);
-        const u32x4 p0 = p[0], p1 = p[1], p2 = p[2], p3 = p[3];
-        c0 = i32x8{(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w, (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
-        c1 = i32x8{(int)p2.x, (int)p2.y, (int)p2.z, (int)p2.w, (int)p3.x, (int)p3.y, (int)p3.z, (int)p3.w};
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(a.w8 + srow * KK + q * kVpt);
+#pragma unroll
+        for (int c = 0; c < kG; ++c) {
+            const u32x4 p0 = p[2 * c], p1 = p[2 * c + 1];
+            cd[c] = i32x8{(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w, (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w};
+        }
     } else {
         const float s = is_w ? ws : xs;
         const bool plain = scale_is_plain(s);
-        uint32_t m0b, m1b;
-        c0 = cast32_e4m3(v0, s, plain, &m0b);
-        c1 = cast32_e4m3(v1, s, plain, &m1b);
-        mag = amax_unpack(amax_pk(m0b, m1b));
+        uint32_t mp = 0;
+#pragma unroll
+        for (int c = 0; c < kG; ++c) {
+            uint32_t mc;
+            cd[c] = cast32_e4m3(v[c], s, plain, &mc);
+            mp = amax_pk(mp, mc);
+        }
+        mag = amax_unpack(mp);
     }
     {
+        // 16-byte chunk h of this thread's codes is chunk (kVpt / 16) q + h of the row
         const int sw4 = row & 15;
-        u32x4 *l = reinterpret_cast<u32x4 *>(lds + row * kFam16K);
-        l[(4 * q) ^ sw4] = u32x4{(uint32_t)c0[0], (uint32_t)c0[1], (uint32_t)c0[2], (uint32_t)c0[3]};
-        l[(4 * q + 1) ^ sw4] = u32x4{(uint32_t)c0[4], (uint32_t)c0[5], (uint32_t)c0[6], (uint32_t)c0[7]};
-        l[(4 * q + 2) ^ sw4] = u32x4{(uint32_t)c1[0], (uint32_t)c1[1], (uint32_t)c1[2], (uint32_t)c1[3]};
-        l[(4 * q + 3) ^ sw4] = u32x4{(uint32_t)c1[4], (uint32_t)c1[5], (uint32_t)c1[6], (uint32_t)c1[7]};
+        u32x4 *l = reinterpret_cast<u32x4 *>(lds + row * KK);
+#pragma unroll
+        for (int c = 0; c < kG; ++c) {
+            const int h = (kVpt / 16) * q + 2 * c;
+            l[h ^ sw4] = u32x4{(uint32_t)cd[c][0], (uint32_t)cd[c][1], (uint32_t)cd[c][2], (uint32_t)cd[c][3]};
+            l[(h + 1) ^ sw4] = u32x4{(uint32_t)cd[c][4], (uint32_t)cd[c][5], (uint32_t)cd[c][6], (uint32_t)cd[c][7]};
+        }
     }
     const bool own = is_w ? own_w : own_x;
     if (own && grow < lim) {
-        uint8_t *dst = (is_w ? a.w8 : a.x8) + (int64_t)grow * kFam16K + q * 64;
-        store32_codes(dst, c0);
-        store32_codes(dst + 32, c1);
+        uint8_t *dst = (is_w ? a.w8 : a.x8) + (int64_t)grow * KK + q * kVpt;
+#pragma unroll
+        for (int c = 0; c < kG; ++c) store32_codes(dst + 32 * c, cd[c]);
     }
     float *amax_slot = is_w ? a.w_amax : a.x_amax;
     if (own && amax_slot != nullptr) {
@@ -1362,42 +1373,46 @@ __global__ __launch_bounds__(8 * TILE) void k_linear_fwd_small(const SmallFwdArg
         if (lane == 0 && m != 0u) atomicMax(reinterpret_cast<unsigned int *>(amax_slot), m << 16);
     }
     __syncthreads();
-    // ---- w8_t rows k, columns n0 .. n0 + TILE - 1 from the W tile: thread t transposes the
-    // 4 x 8 byte block k = 4 (t / (TILE / 8)) .., n = 8 (t % (TILE / 8)) ..
+    // ---- w8_t rows k, columns n0 .. n0 + TILE - 1 from the W tile: 4 x 8 byte blocks, block b
+    // = t + 8 TILE i covering k = 4 (b / (TILE / 8)) .., n = 8 (b % (TILE / 8)) ..
     if (own_w) {
-        const int n8 = (t % (TILE / 8)) * 8, k4 = (t / (TILE / 8)) * 4;
-        uint32_t d[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int n = n8 + i;
-            d[i] = *reinterpret_cast<const uint32_t *>(sw + n * kFam16K + (((k4 >> 4) ^ (n & 15)) << 4) + (k4 & 15));
-        }
-        uint32_t o[4], p[4];
-        tr4(d[0], d[1], d[2], d[3], o[0], o[1], o[2], o[3]);
-        tr4(d[4], d[5], d[6], d[7], p[0], p[1], p[2], p[3]);
-        if (n0 + n8 < N) {
+        for (int i = 0; i < KK / 256; ++i) {
+            const int b = t + 8 * TILE * i;
+            const int n8 = (b % (TILE / 8)) * 8, k4 = (b / (TILE / 8)) * 4;
+            uint32_t d[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<u32x2 *>(a.w8_t + (int64_t)(k4 + j) * N + n0 + n8) = u32x2{o[j], p[j]};
+            for (int e = 0; e < 8; ++e) {
+                const int n = n8 + e;
+                d[e] = *reinterpret_cast<const uint32_t *>(sw + n * KK + (((k4 >> 4) ^ (n & 15)) << 4) + (k4 & 15));
+            }
+            uint32_t o[4], p[4];
+            tr4(d[0], d[1], d[2], d[3], o[0], o[1], o[2], o[3]);
+            tr4(d[4], d[5], d[6], d[7], p[0], p[1], p[2], p[3]);
+            if (n0 + n8 < N) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<u32x2 *>(a.w8_t + (int64_t)(k4 + j) * N + n0 + n8) = u32x2{o[j], p[j]};
+            }
         }
     }
-    // ---- the two K steps: lane l supplies row l % 16 of the 16-row x and W slices and K bytes
-    // [32 (l / 16), +32) of each step
+    // ---- the K steps of 128 bytes: lane l supplies row l % 16 of the 16-row x and W slices and
+    // K bytes [32 (l / 16), +32) of each step
     f32x4 acc[kPerWave];
 #pragma unroll
     for (int j = 0; j < kPerWave; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int st = 0; st < KK / kQK; ++st) {
         const int ch = 8 * st + 2 * g;
         const int ra = tm16 * 16 + r16;
-        const u32x4 a0 = *reinterpret_cast<const u32x4 *>(sx + ra * kFam16K + ((ch ^ r16) << 4));
-        const u32x4 a1 = *reinterpret_cast<const u32x4 *>(sx + ra * kFam16K + (((ch + 1) ^ r16) << 4));
+        const u32x4 a0 = *reinterpret_cast<const u32x4 *>(sx + ra * KK + ((ch ^ r16) << 4));
+        const u32x4 a1 = *reinterpret_cast<const u32x4 *>(sx + ra * KK + (((ch + 1) ^ r16) << 4));
         const i32x8 fa = i32x8{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
 #pragma unroll
         for (int j = 0; j < kPerWave; ++j) {
             const int rb = (tn16 + j) * 16 + r16;
-            const u32x4 b0 = *reinterpret_cast<const u32x4 *>(sw + rb * kFam16K + ((ch ^ r16) << 4));
-            const u32x4 b1 = *reinterpret_cast<const u32x4 *>(sw + rb * kFam16K + (((ch + 1) ^ r16) << 4));
+            const u32x4 b0 = *reinterpret_cast<const u32x4 *>(sw + rb * KK + ((ch ^ r16) << 4));
+            const u32x4 b1 = *reinterpret_cast<const u32x4 *>(sw + rb * KK + (((ch + 1) ^ r16) << 4));
             const i32x8 fb = i32x8{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
             acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa, acc[j], kE4M3, kE4M3, 0, 0, 0, 0);
         }
@@ -1525,21 +1540,26 @@ hipError_t launch_gemm_bias(const uint8_t *A, int fa, const float *a_sinv, int64
     return hipGetLastError();
 }
 
-// The one-launch small forward takes K == 256 (a block casts a row's 256 values in one pass), no
-// x transpose, N % 16 == 0 (whole 8-byte groups of w8_t rows), at most 256 blocks of 64 x 64 and
-// fewer than 40 tiles of 256 x 256 (the GEMM of the two-launch form is then k_gemm_small16, whose
-// bits it reproduces).  Measured through the C ABI, back to back, against the cast-pair launch +
-// GEMM launch: [1024, 1024, 256] 6.2 against 8.5 us; beyond 256 blocks the two are close
-// ([768, 1536, 256] 9.1 against 9.4 us) and then the two launches win ([1024, 2048, 256] 10.1
-// against 9.7 us).  Up to 128 blocks of 64 x 64 the 32 x 32 tiles are faster ([128, 256, 256]
-// 4.2 against 5.7 us, [512, 1024, 256] 5.3 against 6.0 us), beyond it the 64 x 64 tiles
-// ([768, 768, 256] 6.0 against 6.4 us, [1024, 1024, 256] 6.2 against 8.3 us).
+// The one-launch small forward takes K = 256, 512 or 1024 (a block casts a row's K values in one
+// pass), no x transpose, N % 16 == 0 (whole 8-byte groups of w8_t rows), at most 256 x 256 / K
+// blocks of 64 x 64 and fewer than 40 tiles of 256 x 256 (the GEMM of the two-launch form is
+// then k_gemm_small16, whose bits it reproduces).  Measured through the C ABI, back to back,
+// against the cast-pair launch + GEMM launch: [1024, 1024, 256] 6.2 against 8.5 us, beyond 256
+// blocks close ([768, 1536, 256] 9.1 against 9.4 us), then the two launches win ([1024, 2048,
+// 256] 10.1 against 9.7 us); K = 512: [128, 256, 512] 6.2 against 9.7 us, [512, 1024, 512]
+// (128 blocks) 8.6 against 9.9 us, [1024, 1024, 512] 10.7 against 10.5 us; K = 1024: [512, 512,
+// 1024] (64 blocks) 10.5 against 11.8 us, [1024, 1024, 1024] 19.5 against 13.2 us.  Up to 128
+// blocks of 64 x 64 the 32 x 32 tiles are faster ([128, 256, 256] 4.2 against 5.7 us,
+// [512, 1024, 256] 5.3 against 6.0 us), beyond it the 64 x 64 tiles ([768, 768, 256] 6.0 against
+// 6.4 us, [1024, 1024, 256] 6.2 against 8.3 us).
 constexpr int64_t kSmallFwdMaxBlocks = 256;
 constexpr int64_t kTinyMaxBlocks64 = 128;
 constexpr int64_t kSmallFwdMaxTiles = 39;
 bool linear_fwd_small_ok(int64_t M, int64_t N, int64_t K, const uint8_t *x8_t) {
-    if (x8_t != nullptr || M <= 0 || N <= 0 || K != kFam16K || N % 16 != 0) return false;
-    if (((M + kSmallTile - 1) / kSmallTile) * ((N + kSmallTile - 1) / kSmallTile) > kSmallFwdMaxBlocks) return false;
+    if (x8_t != nullptr || M <= 0 || N <= 0 || N % 16 != 0) return false;
+    if (K != 256 && K != 512 && K != 1024) return false;
+    const int64_t blocks64 = ((M + kSmallTile - 1) / kSmallTile) * ((N + kSmallTile - 1) / kSmallTile);
+    if (blocks64 * K > kSmallFwdMaxBlocks * 256) return false;   // 256, 128, 64 blocks for K = 256, 512, 1024
     return ((M + BM - 1) / BM) * ((N + BN - 1) / BN) <= kSmallFwdMaxTiles;
 }
 
@@ -1554,15 +1574,18 @@ hipError_t launch_linear_fwd_small(const uint16_t *x, const uint16_t *w, const u
     a.x8 = x8; a.w8 = w8; a.w8_t = w8_t; a.y = y;
     a.M = (int)M; a.N = (int)N; a.K = (int)K;
     const int64_t blocks64 = ((M + kSmallTile - 1) / kSmallTile) * ((N + kSmallTile - 1) / kSmallTile);
-    if (blocks64 <= kTinyMaxBlocks64) {
-        a.tiles_n = (int)((N + 31) / 32);
-        const dim3 grid((unsigned)a.tiles_n, (unsigned)((M + 31) / 32));
-        k_linear_fwd_small<32><<<grid, dim3(256), 0, st>>>(a);
-    } else {
-        a.tiles_n = (int)((N + 63) / 64);
-        const dim3 grid((unsigned)a.tiles_n, (unsigned)((M + 63) / 64));
-        k_linear_fwd_small<64><<<grid, dim3(512), 0, st>>>(a);
-    }
+#define FP8DS_SMALL_FWD(TILE_, KK_)                                                                        \
+    do {                                                                                                   \
+        a.tiles_n = (int)((N + TILE_ - 1) / TILE_);                                                        \
+        const dim3 grid((unsigned)a.tiles_n, (unsigned)((M + TILE_ - 1) / TILE_));                         \
+        k_linear_fwd_small<TILE_, KK_><<<grid, dim3(8 * TILE_), 0, st>>>(a);                               \
+    } while (0)
+    // (K = 512 and 1024 stay within 128 blocks of 64 x 64 by the rule, so they take 32 x 32 tiles)
+    if (K == 256 && blocks64 > kTinyMaxBlocks64) FP8DS_SMALL_FWD(64, 256);
+    else if (K == 256) FP8DS_SMALL_FWD(32, 256);
+    else if (K == 512) FP8DS_SMALL_FWD(32, 512);
+    else FP8DS_SMALL_FWD(32, 1024);
+#undef FP8DS_SMALL_FWD
     return hipGetLastError();
 }
 

@@ -272,8 +272,8 @@ int fp8_transpose(const uint8_t *in, int64_t rows, int64_t cols, uint8_t *out_t,
  *   3. y = gemm_bias(x8, w8) with *x_scale_inv, *w_scale_inv and bias.
  * Steps 1 and 2 are one kernel launch when both tensors take the same cast code path (M and N
  * both multiples of 16 with K a multiple of 8, or neither), else two.  A small layer (x8_t
- * NULL, K == 256, N % 16 == 0, at most 256 output blocks of 64 x 64 and fewer than 40 of
- * 256 x 256) runs all three steps as one launch, in which each block casts the x and W rows of
+ * NULL, K = 256, 512 or 1024, N % 16 == 0, at most 256 x 256 / K output blocks of 64 x 64 and
+ * fewer than 40 of 256 x 256) runs all three steps as one launch, in which each block casts the x and W rows of
  * its output tile (32 x 32 tiles up to 128 blocks of 64 x 64, 64 x 64 tiles beyond).  The
  * results are those of the separate calls in every case, bit for bit.
  * x: [M, K], W: [N, K], bias: [N] or NULL (bfloat16).  x8: [M, K], x8_t: [K, M] or NULL,

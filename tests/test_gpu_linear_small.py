@@ -1,6 +1,6 @@
-"""The one-launch forward of small layers (fp8_linear_fwd when K == 256, N % 16 == 0, no x
-transpose, at most 256 output blocks of 64 x 64 and fewer than 40 of 256 x 256; 32 x 32 tiles up
-to 128 blocks of 64 x 64) against the
+"""The one-launch forward of small layers (fp8_linear_fwd when K is 256, 512 or 1024, N % 16 ==
+0, no x transpose, at most 256 x 256 / K output blocks of 64 x 64 and fewer than 40 of 256 x 256;
+32 x 32 tiles up to 128 blocks of 64 x 64) against the
 individual calls (cast of x, cast+transpose of W, GEMM + bias: every output bit for bit) and
 against the oracle (codes, amaxes and inverse scales exact, y within the GEMM tolerance),
 including the cached-weight flag, non-finite inputs, scales that are not plain, graph replay, and
@@ -50,11 +50,13 @@ def _equal(a, b):
     assert torch.equal(a.y.view(torch.int16), b.y.view(torch.int16))
 
 
-# the small layer [128, 256] x [256, 256], a ragged M, a narrow N, a wide N, the largest block
-# count (16 x 16 blocks of 64 x 64); then layers outside the rule: K = 512 and 8192, 288 blocks
+# the small layer [128, 256] x [256, 256], a ragged M, a narrow N, a wide N, both tile sizes and
+# the largest block count (16 x 16 blocks of 64 x 64); K = 512 and 1024 inside their block
+# limits; then layers outside the rule: K = 512 at 256 blocks, K = 8192, 288 blocks
 @pytest.mark.parametrize("shape", [(128, 256, 256), (100, 48, 256), (64, 1024, 256), (130, 16, 256), (512, 1024, 256),
                                    (1024, 768, 256), (1024, 832, 256), (1024, 1024, 256),
-                                   (100, 48, 512), (130, 16, 8192), (768, 1536, 256)])
+                                   (100, 48, 512), (512, 1024, 512), (130, 16, 1024), (512, 512, 1024),
+                                   (1024, 1024, 512), (130, 16, 8192), (768, 1536, 256)])
 @pytest.mark.parametrize("with_bias", [True, False])
 def test_one_launch_equals_primitives_and_oracle(shape, with_bias):
     M, N, K = shape
@@ -78,7 +80,7 @@ def test_one_launch_equals_primitives_and_oracle(shape, with_bias):
     gemm_close(to_f64(a.y), fw["y"], bf16_out=True)
 
 
-@pytest.mark.parametrize("shape", [(128, 256, 256), (1024, 1024, 256)])
+@pytest.mark.parametrize("shape", [(128, 256, 256), (1024, 1024, 256), (128, 256, 1024)])
 @pytest.mark.parametrize("xs, ws", [(0.0, 1.0), (float("inf"), 2.0), (1.0, 1e30)])
 def test_one_launch_specials(xs, ws, shape):
     """Infinities, NaNs and saturating values in x and W, a zero or infinite x scale, a weight
@@ -130,7 +132,7 @@ def test_one_launch_without_amax_slots(shape):
     assert not torch.any(a.am)    # untouched
 
 
-@pytest.mark.parametrize("shape", [(128, 256, 256), (1024, 1024, 256)])
+@pytest.mark.parametrize("shape", [(128, 256, 256), (1024, 1024, 256), (128, 256, 512)])
 def test_one_launch_cached_weight_and_graph(shape):
     """With the weight's flag at 1 the layer multiplies by the cached codes and inverse scale and
     writes nothing of W (a changed bfloat16 W is not seen); captured once and replayed with the
@@ -176,14 +178,17 @@ def test_one_launch_cached_weight_and_graph(shape):
         gemm_close(to_f64(a.y), fw["y"], bf16_out=True)
 
 
-@pytest.mark.parametrize("shape, one", [((128, 256, 256), "k_linear_fwd_small<32>"),
-                                        ((512, 1024, 256), "k_linear_fwd_small<32>"),
-                                        ((768, 768, 256), "k_linear_fwd_small<64>"),
-                                        ((1024, 1024, 256), "k_linear_fwd_small<64>"), ((128, 256, 512), None),
+@pytest.mark.parametrize("shape, one", [((128, 256, 256), "k_linear_fwd_small<32, 256>"),
+                                        ((512, 1024, 256), "k_linear_fwd_small<32, 256>"),
+                                        ((768, 768, 256), "k_linear_fwd_small<64, 256>"),
+                                        ((1024, 1024, 256), "k_linear_fwd_small<64, 256>"),
+                                        ((128, 256, 512), "k_linear_fwd_small<32, 512>"),
+                                        ((512, 512, 1024), "k_linear_fwd_small<32, 1024>"),
+                                        ((1024, 1024, 512), None), ((1024, 1024, 1024), None), ((128, 256, 768), None),
                                         ((768, 1536, 256), None)])
 def test_dispatch_rule_launches(shape, one):
-    """Inside the rule the forward is a single launch: k_linear_fwd_small<32> (32 x 32 tiles) up
-    to 128 blocks of 64 x 64, k_linear_fwd_small<64> beyond; outside it the cast launch and the GEMM
+    """Inside the rule the forward is a single launch of k_linear_fwd_small<TILE, K> (32 x 32
+    tiles up to 128 blocks of 64 x 64, 64 x 64 beyond); outside it the cast launch and the GEMM
     launch (all give the same bits; this checks which one ran)."""
     M, N, K = shape
     x = bf16_dev(S.normal_bf16(S.seed_for(9, 30), (M, K), 1.0))
