@@ -1211,16 +1211,16 @@ __global__ __launch_bounds__(64) void k_gemm_small16(const uint8_t *__restrict__
 }
 
 // ------------------------------------------------------------------------------------------
-// k_linear_fwd_small<TILE>: the forward of a small FP8 linear layer in one launch.  At the size
-// of a [128, 256] x [256, 256] layer both kernels of the two-launch form are pure latency (a cast
-// launch of two tiles, then eight waves of GEMM), so here each TILE x TILE output tile's block
-// (TILE 32 or 64, 8 TILE threads) casts the bfloat16 rows it multiplies itself.  K is 256, so a
-// block casts every row it needs in one pass: the first 4 TILE threads the tile's x rows, the
-// others its W rows, each thread 64 consecutive K values (four per row); the codes go to two
-// TILE x 256-byte LDS tiles (16-byte chunk c of row r at chunk c ^ (r % 16)).  After one barrier
-// each wave multiplies TILE / 32 of the 16 x 16 output tiles (one x slice, TILE / 32 adjacent W
-// slices) with the two 128-byte K steps of k_gemm_small16 in its order, on the same fragments,
-// so y is identical.  The casts' outputs are written by the blocks that own them: tile column 0
+// k_linear_fwd_small<TILE, K>: the forward of a small FP8 linear layer in one launch.  At the
+// size of a [128, 256] x [256, 256] layer both kernels of the two-launch form are pure latency (a
+// cast launch of two tiles, then eight waves of GEMM), so here each TILE x TILE output tile's
+// block (TILE 32 or 64, 8 TILE threads) casts the bfloat16 rows it multiplies itself.  K is 256,
+// 512 or 1024, so a block casts every row it needs in one pass: the first 4 TILE threads the
+// tile's x rows, the others its W rows, each thread K / 4 consecutive K values (four threads per
+// row); the codes go to two TILE x K-byte LDS tiles (16-byte chunk c of row r at chunk
+// c ^ (r % 16)).  After one barrier each wave multiplies TILE / 32 of the 16 x 16 output tiles
+// (one x slice, TILE / 32 adjacent W slices) with the K / 128 steps of k_gemm_small16 in its
+// order, on the same fragments, so y is identical.  The casts' outputs are written by the blocks that own them: tile column 0
 // writes x8 and folds x's amax; tile row 0 writes w8, folds W's amax and writes w8_t from the W
 // tile with 4 x 4 byte register transposes.  A cached weight (*w_noop == 1) is read as codes
 // from w8 and nothing of W is written.  Every code equals the cast kernels' (same clamp +
